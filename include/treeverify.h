@@ -1,0 +1,234 @@
+/*
+ * treeverify.h -- C ABI of libtreeverify.so: one tree-verification round of
+ * speculative decoding on an AMD Instinct MI355X (gfx950).
+ *
+ * A round has three calls, in this order on one stream:
+ *   tv_tree_build            draft marginals -> prefix-closed draft tree
+ *   tv_tree_attention_verify tree-masked attention of the target over
+ *                            context + tree (one layer)
+ *   tv_tree_accept           acceptance walk -> accepted path + one token
+ * plus tv_tree_ancestors for trees that come from elsewhere.
+ *
+ * Conventions shared by every call
+ *   - Every array argument is a DEVICE pointer owned by the caller, dense
+ *     and row-major in the layout given in its comment.  The library
+ *     allocates and frees nothing; scratch space is the caller's
+ *     `workspace` of at least the size the matching *_workspace() returns.
+ *   - Calls are asynchronous on `stream`: they enqueue kernels and return
+ *     without synchronising.  The library keeps no global mutable state, so
+ *     calls from several host threads on different streams are safe.
+ *   - Arguments are checked on the host before any launch; a bad argument
+ *     returns TV_ERR_INVALID (or TV_ERR_UNSUPPORTED for a valid request this
+ *     build does not serve) and launches nothing.  A launch failure
+ *     reported by the HIP runtime returns TV_ERR_DEVICE.  Nothing throws
+ *     across this boundary.
+ *   - Device-side data (tree arrays, token ids, lengths) are preconditions;
+ *     the kernels stay in bounds for any values, but results for values
+ *     that break a stated precondition are unspecified.
+ *   - Results are deterministic: the same inputs give the same bits.
+ *
+ * Numerics of the integer decisions (tree shape, accepted length, sampled
+ * tokens), identical on every run:
+ *   - A logit l of a row with maximum m at inverse temperature 1/T has the
+ *     fixed-point weight W = rint(exp32(fl32(fl32(l - m) * fl32(1/T))) * 2^44),
+ *     where exp32 is an fp32 Cody-Waite reduction (ln 2 split in two parts,
+ *     the high part with 12 significand bits) followed by the degree-7
+ *     Taylor polynomial of e^r in Horner form with fused multiply-adds, and
+ *     is 0 below -32.  Row sums Z = sum W are exact 64-bit integers.
+ *   - Draft probabilities are q = fp64(W) / fp64(Z); path scores are fp64
+ *     products taken from the root down.
+ *   - Random draws use Philox4x64-10 with key (seed, 0) and counter
+ *     (round, sequence, node, slot).
+ */
+#ifndef TREEVERIFY_H
+#define TREEVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TV_OK = 0,
+    TV_ERR_INVALID = 1,     /* bad pointer, size or combination of arguments */
+    TV_ERR_UNSUPPORTED = 2, /* valid, but outside what this build serves      */
+    TV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required     */
+    TV_ERR_DEVICE = 4       /* the HIP runtime reported a launch error        */
+} tv_status;
+
+typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
+typedef enum { TV_GREEDY = 0, TV_SAMPLED = 1 } tv_accept_mode;
+typedef enum { TV_PROPOSAL_POINT_MASS = 0, TV_PROPOSAL_DRAFT = 1 } tv_proposal;
+
+/* Limits of this build. */
+#define TV_MAX_VOCAB (1 << 18)
+#define TV_MAX_TOPK 64
+#define TV_MAX_BUDGET 1023
+#define TV_MAX_POSITIONS 64
+
+/* Human-readable name of a status code (static storage). */
+const char *tv_status_string(tv_status s);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int tv_version(void);
+
+/* ------------------------------------------------------------------------
+ * tv_tree_build -- draft tree from per-position draft marginals.
+ *
+ * TAPS sec. 4.1: the drafter gives marginal logits for K future positions
+ * in one pass; the top-`topk` tokens of each position form the candidate
+ * tree (position j's candidates are the children of every depth j-1 node).
+ * TAPS sec. 4.2 and TreeGraft sec. 3.1: each edge carries the drafter's
+ * probability q of the child's token at its position; a node's reach
+ * probability is the product of the edge probabilities from the root, and
+ * the root (the verified prefix) has probability 1.  TAPS sec. 1 / 3.2: a
+ * compact prefix-closed subtree that maximises the expected number of
+ * accepted tokens under the node budget -- the `budget` nodes of largest
+ * reach probability.
+ *
+ * Candidates of a position are its top-`topk` tokens by (logit desc, id asc),
+ * ranked by (q desc, id asc); q uses temperature `build_temp`.  Nodes are
+ * chosen in the total order (score desc, depth asc, parent earlier in this
+ * order, rank asc) and written in that order: row 0 is the root, rows
+ * 1..n-1 the chosen nodes, n = n_nodes[b] = 1 + min(budget, number of
+ * candidate-tree nodes).  Every parent row precedes its children.
+ *
+ *   draft_logits  [batch][K][V], dtype dt (f32 or bf16); finite values, or
+ *                 -inf with a finite row maximum.
+ *   root_token    [batch] token of the root (the last verified token)
+ *   ctx_len       [batch] context length L_b already in the KV cache
+ *   parent, token, depth, pos   int32 [batch][budget+1]
+ *                 parent row (-1 for the root), token id, depth (root 0),
+ *                 position id L_b + depth (PTD sec. 3.1: a node's position
+ *                 follows from the size of its ancestor set).
+ *   score         double [batch][budget+1] reach probability (root 1.0)
+ *   anc_mask      uint64 [batch][budget+1][ceil((budget+1)/64)]: bit j of
+ *                 row i is set iff node j is i or an ancestor of i.
+ *   n_nodes       int32 [batch]
+ *   Rows past n_nodes: parent = token = depth = pos = -1, score 0, mask 0.
+ * Limits: 1 <= K <= 64, 1 <= topk <= min(64, V), V <= 2^18, 0 <= budget <= 1023,
+ *   build_temp > 0, K * topk <= 4096.
+ * ------------------------------------------------------------------------ */
+size_t tv_tree_build_workspace(int batch, int K, int V, int topk, int budget);
+tv_status tv_tree_build(const void *draft_logits, tv_dtype dt, int batch, int K, int V,
+                        int topk, int budget, float build_temp, const int32_t *root_token,
+                        const int32_t *ctx_len, int32_t *parent, int32_t *token,
+                        int32_t *depth, int32_t *pos, double *score, uint64_t *anc_mask,
+                        int32_t *n_nodes, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * tv_tree_ancestors -- depth, position ids and ancestor bit rows of trees
+ * given as parent arrays (PTD sec. 3.1: pi(v) = {v} U pi(P(v))).
+ *
+ *   parent   int32 [batch][N]; parent[0] = -1, 0 <= parent[i] < i for
+ *            1 <= i < n_nodes[b] (precondition).
+ *   n_nodes  int32 [batch], 1 <= n_nodes[b] <= N.
+ *   ctx_len  int32 [batch].
+ *   depth, pos  int32 [batch][N];  anc_mask uint64 [batch][N][ceil(N/64)].
+ *   Rows past n_nodes: depth = pos = -1, mask 0.
+ * Limits: 1 <= N <= 1024.  No workspace.
+ * ------------------------------------------------------------------------ */
+tv_status tv_tree_ancestors(const int32_t *parent, const int32_t *n_nodes,
+                            const int32_t *ctx_len, int batch, int N, int32_t *depth,
+                            int32_t *pos, uint64_t *anc_mask, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * tv_tree_attention_verify -- one target attention layer over context +
+ * tree in a single pass.
+ *
+ * Primer, "why the target can verify in parallel": the target reads the
+ * original context followed by the draft tokens in one forward pass.  PTD
+ * sec. 3.1: a tree node attends only to its ancestor set pi(v).  So node i of
+ * sequence b, query head h, attends to the cached context keys [0, L_b) and
+ * to the tree keys at cache rows L_b + j for every j in pi(i); GQA maps
+ * query head h to KV head h / (Hq / Hkv).  out = softmax((q . k) * scale) v,
+ * lse = natural log of the softmax normaliser (max included).
+ *
+ *   q        [batch][N][Hq][D]       dtype dt
+ *   k_cache, v_cache [batch][Hkv][cap][D]  dtype dt; context rows [0, L_b),
+ *            tree rows at L_b + i (the target layer writes them there).
+ *   ctx_len  int32 [batch], 0 <= L_b <= max_ctx (precondition)
+ *   anc_mask uint64 [batch][N][ceil(N/64)] as written by tv_tree_build
+ *   n_nodes  int32 [batch], 1 <= n_nodes[b] <= N (precondition)
+ *   out      [batch][N][Hq][D]       dtype dt
+ *   lse      float [batch][N][Hq], may be NULL
+ *   splits   number of context splits (0 = automatic); partial results are
+ *            merged with their log-sum-exp weights.
+ *   Rows past n_nodes: out 0, lse -inf.
+ * Limits: D in {64, 128}; Hq % Hkv == 0; N <= 1024; max_ctx + N <= cap.
+ * bf16: bf16 products on the matrix cores with fp32 accumulation and an
+ * fp32 online softmax.  f32: fp32 throughout (vector ALU).
+ * ------------------------------------------------------------------------ */
+size_t tv_tree_attention_workspace(int batch, int N, int Hq, int Hkv, int D, int max_ctx,
+                                   int splits);
+tv_status tv_tree_attention_verify(const void *q, const void *k_cache, const void *v_cache,
+                                   tv_dtype dt, const int32_t *ctx_len,
+                                   const uint64_t *anc_mask, const int32_t *n_nodes,
+                                   int batch, int N, int Hq, int Hkv, int D, int cap,
+                                   int max_ctx, float scale, int splits, void *out,
+                                   float *lse, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * tv_tree_accept -- the acceptance walk over one tree per sequence.
+ *
+ * Primer, "acceptance and rejection": starting at the root, greedy mode
+ * follows the child whose token equals the target's argmax (lowest id on
+ * ties; the first such child in row order) until none does, then emits the
+ * target's argmax.  Sampled mode at temperature T:
+ *   TV_PROPOSAL_POINT_MASS (trees of deterministic candidates, e.g. from
+ *     tv_tree_build): at node u the children are tried in row order; child
+ *     with token t is accepted with probability min(1, p_res(t) / 1), where
+ *     p_res is the target's distribution at u with the tokens of the
+ *     already rejected siblings removed and renormalised; if all are
+ *     rejected (or u is a leaf) one token is drawn from p_res.  The emitted
+ *     sequence has exactly the target's autoregressive law.
+ *   TV_PROPOSAL_DRAFT (chains whose tokens were sampled from the drafter):
+ *     child token t at depth d is accepted with probability min(1, p(t) /
+ *     q_d(t)), q_d the drafter's distribution at position d (draft row d-1);
+ *     at the first rejection one token is drawn from (p - q_d)+ normalised.
+ *     A node with more than one child sets accept_len[b] = -1.
+ * The round emits the accepted drafts and one more token.
+ *
+ * Draws: acceptance of the i-th child of node u uses Philox word 0 of
+ * counter (round, b, u, i); the final draw at node u uses words 0 and 1 of
+ * counter (round, b, u, 0xFFFFFFFF) as a 128-bit uniform and an exact
+ * integer inverse CDF over the weights.  POINT_MASS accepts iff
+ * U * Z_res < W(t) * 2^64 (exact).  DRAFT accepts iff p >= q or
+ * (U >> 11) * 2^-53 < p / q in fp64, and its residual weights are
+ * rint(max(0, p - q) * 2^62).
+ *
+ *   target_logits [batch][N][V]   dtype dt; row i = the target's next-token
+ *                                 logits after node i's prefix.
+ *   draft_logits  [batch][K][V]   DRAFT only (else NULL); row j = position j+1.
+ *   parent, token, depth  int32 [batch][N]; n_nodes int32 [batch].
+ *   accept_len     int32 [batch]  accepted drafted tokens (or -1, see above)
+ *   accepted_nodes int32 [batch][max_depth+1]: root row 0, then the rows of
+ *                  the accepted nodes, then -1.
+ *   out_tokens     int32 [batch][max_depth+1]: the accepted tokens, then
+ *                  the emitted token, then -1.
+ * A node at depth max_depth is treated as a leaf.  Tokens outside [0, V)
+ * are never accepted.
+ * Limits: V <= 2^18; N <= 1024; 1 <= max_depth <= 1023; temperature > 0 in
+ * sampled mode; K >= 1 with draft_logits in DRAFT mode.
+ * ------------------------------------------------------------------------ */
+size_t tv_tree_accept_workspace(int batch, int N, int K, int V, tv_accept_mode mode,
+                                tv_proposal proposal);
+tv_status tv_tree_accept(const void *target_logits, const void *draft_logits, tv_dtype dt,
+                         int batch, int N, int K, int V, const int32_t *parent,
+                         const int32_t *token, const int32_t *depth, const int32_t *n_nodes,
+                         tv_accept_mode mode, float temperature, tv_proposal proposal,
+                         uint64_t seed, uint64_t round, int max_depth, int32_t *accept_len,
+                         int32_t *accepted_nodes, int32_t *out_tokens, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREEVERIFY_H */

@@ -573,17 +573,16 @@ static int children_of(const int32_t *parent, int n, int u, int32_t *out)
     return c;
 }
 
-static int accept_one(const float *target, const float *draft, int N, int V,
+static int accept_one(const float *target, const float *draft, int N, int K, int V,
                       const int32_t *parent, const int32_t *token, const int32_t *depth, int n,
                       int mode, float temperature, int proposal, uint64_t seed, uint64_t round,
                       uint64_t seq, int max_depth, int32_t *accept_len, int32_t *acc_nodes,
                       int32_t *out_tokens)
 {
-    (void)N;
     const int width = max_depth + 1;
     for (int i = 0; i < width; ++i) { acc_nodes[i] = -1; out_tokens[i] = -1; }
-    *accept_len = 0;
-    if (n < 1) return TVO_ERR;
+    *accept_len = -1;
+    if (n < 1 || n > N) return TVO_ERR; /* needs a root and at most N rows */
     acc_nodes[0] = 0;
     int32_t *kids = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
     uint64_t *W = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)V);
@@ -646,7 +645,7 @@ static int accept_one(const float *target, const float *draft, int N, int V,
         int c = kids[0];
         int t = token[c];
         int d = depth[c];
-        if (d < 1 || !draft) { rc = TVO_ERR; break; }
+        if (d < 1 || d > K || !draft) { rc = TVO_ERR; break; }
         const float *qrow = draft + (size_t)(d - 1) * V;
         uint64_t Zq = tvo_row_weights(qrow, V, inv_t, Wq);
         double pt = (t >= 0 && t < V) ? (double)W[t] / (double)Z : 0.0;
@@ -701,7 +700,7 @@ int tvo_tree_accept(const float *target, const float *draft, int batch, int N, i
     const int width = max_depth + 1;
     for (int b = 0; b < batch; ++b) {
         const float *dr = draft ? draft + (size_t)b * K * V : NULL;
-        int r = accept_one(target + (size_t)b * N * V, dr, N, V, parent + (size_t)b * N,
+        int r = accept_one(target + (size_t)b * N * V, dr, N, K, V, parent + (size_t)b * N,
                            token + (size_t)b * N, depth + (size_t)b * N, n_nodes[b], mode,
                            temperature, proposal, seed, round, (uint64_t)b, max_depth,
                            accept_len + b, accepted_nodes + (size_t)b * width,

@@ -1,0 +1,119 @@
+"""GPU parity of tv_tree_attention_verify with the fp64 oracle: max abs error
+<= 1e-2 and norm-wise relative error <= 2e-2 per sequence (bf16 inputs,
+fp32 accumulation), plus determinism at a fixed split count."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_verification_best_amd as tv
+import workloads
+from gpu_util import assert_attention_close, bf16_dev, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _tree(r, kind, n, N):
+    parent = np.full(N, -1, np.int32)
+    for i in range(1, n):
+        if kind == "chain":
+            parent[i] = i - 1
+        elif kind == "star":
+            parent[i] = 0
+        else:
+            parent[i] = r.integers(0, i)
+    anc = np.zeros((N, (N + 63) // 64), np.uint64)
+    anc[:n] = oracle.ancestors(parent[:n], words=(N + 63) // 64)[0]
+    return parent, anc
+
+
+def _case(seed, b, N, Hq, Hkv, D, Ls, ns, kind="random", dtype="bf16", splits=0):
+    r = np.random.default_rng(seed)
+    cap = max(Ls) + N + 5
+    q = r.standard_normal((b, N, Hq, D)).astype(np.float32)
+    k = r.standard_normal((b, Hkv, cap, D)).astype(np.float32)
+    v = r.standard_normal((b, Hkv, cap, D)).astype(np.float32)
+    if dtype == "bf16":
+        q, k, v = workloads.round_bf16(q), workloads.round_bf16(k), workloads.round_bf16(v)
+    anc = np.stack([_tree(r, kind, ns[s], N)[1] for s in range(b)])
+    ctx = np.array(Ls, np.int32)
+    nn = np.array(ns, np.int32)
+    put = bf16_dev if dtype == "bf16" else dev
+    out, lse = tv.tv_tree_attention_verify(put(q), put(k), put(v), dev(ctx),
+                                           dev(anc.view(np.int64)), dev(nn), max(Ls),
+                                           splits=splits)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.tree_attention(q, k, v, ctx, anc, nn)
+    return out, lse, ref_out, ref_lse, nn
+
+
+CASES = [
+    # name, b, N, Hq, Hkv, D, Ls, ns, kind, dtype, splits
+    ("tiny-f32", 1, 17, 1, 1, 64, [128], [17], "random", "f32", 0),
+    ("f32-gqa", 2, 20, 4, 2, 128, [70, 0], [20, 13], "random", "f32", 0),
+    ("bf16-d128", 1, 20, 4, 2, 128, [100], [20], "random", "bf16", 0),
+    ("bf16-d64", 1, 33, 8, 8, 64, [257], [30], "random", "bf16", 0),
+    ("chain", 1, 40, 4, 1, 128, [64], [40], "chain", "bf16", 0),
+    ("star", 1, 40, 4, 4, 128, [33], [40], "star", "bf16", 0),
+    ("no-context", 1, 24, 8, 2, 128, [0], [24], "random", "bf16", 0),
+    ("ragged-batch", 3, 33, 8, 2, 128, [1000, 37, 513], [33, 1, 20], "random", "bf16", 0),
+    ("one-split", 1, 65, 8, 2, 128, [700], [65], "random", "bf16", 1),
+    ("many-splits", 1, 65, 8, 2, 128, [700], [65], "random", "bf16", 7),
+    ("4b-heads", 1, 65, 32, 8, 128, [4096], [65], "random", "bf16", 0),
+    ("wide-tree", 1, 257, 8, 2, 128, [300], [257], "random", "bf16", 0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_attention(case):
+    name, b, N, Hq, Hkv, D, Ls, ns, kind, dt, splits = case
+    out, lse, ro, rl, nn = _case(zlib.crc32(name.encode()), b, N, Hq, Hkv, D, Ls, ns, kind, dt,
+                                 splits)
+    assert_attention_close(out, lse, ro, rl, nn, name)
+
+
+def test_attention_deterministic():
+    r = np.random.default_rng(3)
+    b, N, Hq, Hkv, D, L = 1, 65, 32, 8, 128, 2000
+    cap = L + N
+    q = bf16_dev(r.standard_normal((b, N, Hq, D)).astype(np.float32))
+    k = bf16_dev(r.standard_normal((b, Hkv, cap, D)).astype(np.float32))
+    v = bf16_dev(r.standard_normal((b, Hkv, cap, D)).astype(np.float32))
+    parent = np.concatenate([[-1], r.integers(0, np.arange(1, N))]).astype(np.int32)
+    anc = oracle.ancestors(parent)[0][None]
+    args = (q, k, v, dev(np.array([L], np.int32)), dev(anc.view(np.int64)),
+            dev(np.array([N], np.int32)), L)
+    o1, l1 = tv.tv_tree_attention_verify(*args, splits=5)
+    o2, l2 = tv.tv_tree_attention_verify(*args, splits=5)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("cfg", ["8b", "long"])
+def test_attention_full_size_sampled_rows(cfg):
+    """Full-size shapes in the automatic split configuration; the oracle checks
+    a sample of (node, all heads) rows one by one."""
+    c = workloads.CONFIGS[cfg]
+    N, L = c["B"] + 1, c["L"]
+    cap = L + N
+    q, k, v = workloads.qkv(c, 1, N, cap)
+    r = np.random.default_rng(11)
+    parent = np.concatenate([[-1], r.integers(0, np.maximum(1, np.arange(1, N) // 4 + 1))])
+    parent = parent.astype(np.int32)
+    anc = oracle.ancestors(parent)[0][None]
+    ctx = np.array([L], np.int32)
+    nn = np.array([N], np.int32)
+    out, lse = tv.tv_tree_attention_verify(bf16_dev(q), bf16_dev(k), bf16_dev(v), dev(ctx),
+                                           dev(anc.view(np.int64)), dev(nn), L)
+    torch.cuda.synchronize()
+    g = out.float().cpu().numpy()
+    gl = lse.cpu().numpy()
+    rows = [(0, i) for i in (0, 1, N // 3, N // 2, N - 2, N - 1)]
+    ref = oracle.tree_attention_rows(q, k, v, ctx, anc, nn, rows)
+    for (s, i), (ro, rl) in ref.items():
+        d = g[s, i] - ro
+        assert np.abs(d).max() <= 1e-2
+        assert np.linalg.norm(d) / np.linalg.norm(ro) <= 2e-2
+        assert np.abs(gl[s, i] - rl).max() <= 1e-2

@@ -1,0 +1,239 @@
+"""tree_verification_best_amd -- one tree-verification round of speculative
+decoding on an AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libtreeverify.so`` (C ABI in
+``include/treeverify.h``).  Every step of the round runs in the library's HIP
+kernels; this module only checks tensors, allocates outputs and workspaces
+with torch and passes device pointers and the current HIP stream.  There is
+no CPU fallback: if the library is missing or no GPU is present the calls
+raise.
+
+    tv_tree_build            draft marginals -> prefix-closed draft tree
+    tv_tree_ancestors        depth / positions / ancestor rows of a parent array
+    tv_tree_attention_verify tree-masked GQA attention over context + tree
+    tv_tree_accept           greedy or sampled acceptance walk
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBPATH = os.path.join(_HERE, "libtreeverify.so")
+
+TV_OK, TV_ERR_INVALID, TV_ERR_UNSUPPORTED, TV_ERR_WORKSPACE, TV_ERR_DEVICE = range(5)
+TV_F32, TV_BF16 = 0, 1
+TV_GREEDY, TV_SAMPLED = 0, 1
+TV_PROPOSAL_POINT_MASS, TV_PROPOSAL_DRAFT = 0, 1
+
+EXPORTS = ("tv_status_string", "tv_version", "tv_tree_build_workspace", "tv_tree_build",
+           "tv_tree_ancestors", "tv_tree_attention_workspace", "tv_tree_attention_verify",
+           "tv_tree_accept_workspace", "tv_tree_accept")
+
+_lib = None
+
+
+class TreeVerifyError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _load().tv_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{where}: {msg}")
+
+
+def _load():
+    """Load libtreeverify.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBPATH):
+        raise ImportError(f"{LIBPATH} is missing: run `python -m tree_verification_best_amd.build`")
+    L = ctypes.CDLL(LIBPATH)
+    c = ctypes
+    vp, i32, f32, sz, u64 = c.c_void_p, c.c_int, c.c_float, c.c_size_t, c.c_uint64
+    L.tv_status_string.argtypes = [i32]
+    L.tv_status_string.restype = c.c_char_p
+    L.tv_version.argtypes = []
+    L.tv_version.restype = i32
+    L.tv_tree_build_workspace.argtypes = [i32, i32, i32, i32, i32]
+    L.tv_tree_build_workspace.restype = sz
+    L.tv_tree_build.argtypes = [vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp,
+                                vp, vp, vp, vp, sz, vp]
+    L.tv_tree_build.restype = i32
+    L.tv_tree_ancestors.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp]
+    L.tv_tree_ancestors.restype = i32
+    L.tv_tree_attention_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.tv_tree_attention_workspace.restype = sz
+    L.tv_tree_attention_verify.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32,
+                                           i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
+    L.tv_tree_attention_verify.restype = i32
+    L.tv_tree_accept_workspace.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.tv_tree_accept_workspace.restype = sz
+    L.tv_tree_accept.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, f32, i32,
+                                 u64, u64, i32, vp, vp, vp, vp, sz, vp]
+    L.tv_tree_accept.restype = i32
+    _lib = L
+    return L
+
+
+def lib():
+    return _load()
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+def _dev(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU (no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _dt(t):
+    if t.dtype == torch.float32:
+        return TV_F32
+    if t.dtype == torch.bfloat16:
+        return TV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(status, where):
+    if status != TV_OK:
+        raise TreeVerifyError(status, where)
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace, workspace.numel() * workspace.element_size()
+    buf = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    return buf, buf.numel()
+
+
+# --------------------------------------------------------------------------
+# the four calls
+# --------------------------------------------------------------------------
+def tree_build_workspace(batch, K, V, topk, budget):
+    return _load().tv_tree_build_workspace(batch, K, V, topk, budget)
+
+
+def tv_tree_build(draft_logits, topk, budget, root_token, ctx_len, build_temp=1.0,
+                  workspace=None, out=None):
+    """draft_logits [b][K][V] (f32/bf16) -> dict of tree tensors [b][budget+1]."""
+    L = _load()
+    b, K, V = draft_logits.shape
+    dev = draft_logits.device
+    N = budget + 1
+    W = (N + 63) // 64
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = dict(parent=torch.empty((b, N), **i32), token=torch.empty((b, N), **i32),
+                   depth=torch.empty((b, N), **i32), pos=torch.empty((b, N), **i32),
+                   score=torch.empty((b, N), dtype=torch.float64, device=dev),
+                   anc=torch.empty((b, N, W), dtype=torch.int64, device=dev),
+                   n_nodes=torch.empty((b,), **i32))
+    need = L.tv_tree_build_workspace(b, K, V, topk, budget)
+    ws, wsb = _workspace(need, dev, workspace)
+    st = L.tv_tree_build(_dev(draft_logits, "draft_logits"), _dt(draft_logits), b, K, V, topk,
+                         budget, float(build_temp), _dev(root_token, "root_token", torch.int32),
+                         _dev(ctx_len, "ctx_len", torch.int32), _dev(out["parent"], "parent"),
+                         _dev(out["token"], "token"), _dev(out["depth"], "depth"),
+                         _dev(out["pos"], "pos"), _dev(out["score"], "score"),
+                         _dev(out["anc"], "anc"), _dev(out["n_nodes"], "n_nodes"),
+                         ws.data_ptr(), wsb, _stream(dev))
+    _check(st, "tv_tree_build")
+    return out
+
+
+def tv_tree_ancestors(parent, n_nodes, ctx_len, out=None):
+    L = _load()
+    b, N = parent.shape
+    dev = parent.device
+    W = (N + 63) // 64
+    if out is None:
+        out = dict(depth=torch.empty((b, N), dtype=torch.int32, device=dev),
+                   pos=torch.empty((b, N), dtype=torch.int32, device=dev),
+                   anc=torch.empty((b, N, W), dtype=torch.int64, device=dev))
+    st = L.tv_tree_ancestors(_dev(parent, "parent", torch.int32),
+                             _dev(n_nodes, "n_nodes", torch.int32),
+                             _dev(ctx_len, "ctx_len", torch.int32), b, N,
+                             _dev(out["depth"], "depth"), _dev(out["pos"], "pos"),
+                             _dev(out["anc"], "anc"), _stream(dev))
+    _check(st, "tv_tree_ancestors")
+    return out
+
+
+def attention_workspace(batch, N, Hq, Hkv, D, max_ctx, splits=0):
+    return _load().tv_tree_attention_workspace(batch, N, Hq, Hkv, D, max_ctx, splits)
+
+
+def tv_tree_attention_verify(q, k_cache, v_cache, ctx_len, anc_mask, n_nodes, max_ctx,
+                             scale=None, splits=0, want_lse=True, workspace=None, out=None,
+                             lse=None):
+    """q [b][N][Hq][D]; caches [b][Hkv][cap][D] -> (out [b][N][Hq][D], lse [b][N][Hq])."""
+    L = _load()
+    b, N, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((b, N, Hq), dtype=torch.float32, device=dev)
+    need = L.tv_tree_attention_workspace(b, N, Hq, Hkv, D, int(max_ctx), int(splits))
+    ws, wsb = _workspace(need, dev, workspace)
+    st = L.tv_tree_attention_verify(_dev(q, "q"), _dev(k_cache, "k_cache", q.dtype),
+                                    _dev(v_cache, "v_cache", q.dtype), _dt(q),
+                                    _dev(ctx_len, "ctx_len", torch.int32),
+                                    _dev(anc_mask, "anc_mask", torch.int64),
+                                    _dev(n_nodes, "n_nodes", torch.int32), b, N, Hq, Hkv, D, cap,
+                                    int(max_ctx), scale, int(splits), _dev(out, "out", q.dtype),
+                                    _dev(lse, "lse", torch.float32) if lse is not None else None,
+                                    ws.data_ptr(), wsb, _stream(dev))
+    _check(st, "tv_tree_attention_verify")
+    return out, lse
+
+
+def accept_workspace(batch, N, K, V, mode, proposal=TV_PROPOSAL_POINT_MASS):
+    return _load().tv_tree_accept_workspace(batch, N, K, V, mode, proposal)
+
+
+def tv_tree_accept(target_logits, parent, token, depth, n_nodes, *, mode, max_depth,
+                   temperature=1.0, proposal=TV_PROPOSAL_POINT_MASS, seed=0, round=0,
+                   draft_logits=None, workspace=None, out=None):
+    """target_logits [b][N][V] -> dict(accept_len [b], accepted_nodes, out_tokens [b][max_depth+1])."""
+    L = _load()
+    b, N, V = target_logits.shape
+    dev = target_logits.device
+    K = draft_logits.shape[1] if draft_logits is not None else 0
+    width = max_depth + 1
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = dict(accept_len=torch.empty((b,), **i32),
+                   accepted_nodes=torch.empty((b, width), **i32),
+                   out_tokens=torch.empty((b, width), **i32))
+    need = L.tv_tree_accept_workspace(b, N, max(K, 1), V, mode, proposal)
+    ws, wsb = _workspace(need, dev, workspace)
+    dptr = _dev(draft_logits, "draft_logits", target_logits.dtype) if draft_logits is not None else None
+    st = L.tv_tree_accept(_dev(target_logits, "target_logits"), dptr, _dt(target_logits), b, N,
+                          K, V, _dev(parent, "parent", torch.int32),
+                          _dev(token, "token", torch.int32), _dev(depth, "depth", torch.int32),
+                          _dev(n_nodes, "n_nodes", torch.int32), int(mode), float(temperature),
+                          int(proposal), int(seed) & (2 ** 64 - 1), int(round) & (2 ** 64 - 1),
+                          int(max_depth), _dev(out["accept_len"], "accept_len"),
+                          _dev(out["accepted_nodes"], "accepted_nodes"),
+                          _dev(out["out_tokens"], "out_tokens"), ws.data_ptr(), wsb,
+                          _stream(dev))
+    _check(st, "tv_tree_accept")
+    return out

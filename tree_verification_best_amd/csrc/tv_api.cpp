@@ -1,0 +1,166 @@
+// tv_api.cpp -- the C ABI of libtreeverify (declared in include/treeverify.h):
+// host-side argument checks, workspace sizing and launches on the caller's
+// stream.  No call allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "tv_internal.h"
+#include "treeverify.h"
+
+namespace {
+
+constexpr size_t kMaxSelectLds = 64 * 1024;
+constexpr int kMaxGridY = 65535;
+
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
+
+bool build_args_ok(int batch, int K, int V, int topk, int budget) {
+  return batch >= 1 && K >= 1 && K <= TV_MAX_POSITIONS && V >= 1 && V <= TV_MAX_VOCAB &&
+         topk >= 1 && topk <= TV_MAX_TOPK && topk <= V && budget >= 0 &&
+         budget <= TV_MAX_BUDGET && K * topk <= 4096;
+}
+
+bool attn_args_ok(int batch, int N, int Hq, int Hkv, int D, int max_ctx, int splits) {
+  return batch >= 1 && N >= 1 && N <= 1024 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 &&
+         (D == 64 || D == 128) && max_ctx >= 0 && splits >= 0;
+}
+
+bool accept_args_ok(int batch, int N, int V, int max_depth) {
+  return batch >= 1 && N >= 1 && N <= 1024 && V >= 1 && V <= TV_MAX_VOCAB && max_depth >= 1 &&
+         max_depth <= 1023;
+}
+
+tv_status device_status(hipError_t e) { return e == hipSuccess ? TV_OK : TV_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+const char* tv_status_string(tv_status s) {
+  switch (s) {
+    case TV_OK: return "TV_OK";
+    case TV_ERR_INVALID: return "TV_ERR_INVALID: invalid argument";
+    case TV_ERR_UNSUPPORTED: return "TV_ERR_UNSUPPORTED: outside the limits of this build";
+    case TV_ERR_WORKSPACE: return "TV_ERR_WORKSPACE: workspace missing or too small";
+    case TV_ERR_DEVICE: return "TV_ERR_DEVICE: HIP launch error";
+  }
+  return "unknown tv_status";
+}
+
+int tv_version(void) { return 10000; }
+
+// ---------------------------------------------------------------------------
+size_t tv_tree_build_workspace(int batch, int K, int V, int topk, int budget) {
+  if (!build_args_ok(batch, K, V, topk, budget)) return 0;
+  return tvk::build_plan(batch, K, V, topk, budget).workspace;
+}
+
+tv_status tv_tree_build(const void* draft_logits, tv_dtype dt, int batch, int K, int V,
+                        int topk, int budget, float build_temp, const int32_t* root_token,
+                        const int32_t* ctx_len, int32_t* parent, int32_t* token,
+                        int32_t* depth, int32_t* pos, double* score, uint64_t* anc_mask,
+                        int32_t* n_nodes, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  if (!draft_logits || !root_token || !ctx_len || !parent || !token || !depth || !pos ||
+      !score || !anc_mask || !n_nodes)
+    return TV_ERR_INVALID;
+  if (dt != TV_F32 && dt != TV_BF16) return TV_ERR_INVALID;
+  if (!finite_pos(build_temp)) return TV_ERR_INVALID;
+  if (batch < 1 || K < 1 || V < 1 || topk < 1 || topk > V || budget < 0) return TV_ERR_INVALID;
+  if (!build_args_ok(batch, K, V, topk, budget)) return TV_ERR_UNSUPPORTED;
+  const tvk::BuildPlan p = tvk::build_plan(batch, K, V, topk, budget);
+  if (p.C * topk > 256 * tvk::kFinalizeE || p.select_lds > kMaxSelectLds ||
+      p.rows > kMaxGridY)
+    return TV_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < p.workspace) return TV_ERR_WORKSPACE;
+  const float inv_t = 1.0f / build_temp;
+  return device_status(tvk::launch_build(p, draft_logits, dt == TV_BF16, batch, K, V, topk,
+                                         budget, inv_t, root_token, ctx_len, parent, token,
+                                         depth, pos, score, anc_mask, n_nodes, workspace,
+                                         stream));
+}
+
+tv_status tv_tree_ancestors(const int32_t* parent, const int32_t* n_nodes,
+                            const int32_t* ctx_len, int batch, int N, int32_t* depth,
+                            int32_t* pos, uint64_t* anc_mask, hipStream_t stream) {
+  if (!parent || !n_nodes || !ctx_len || !depth || !pos || !anc_mask) return TV_ERR_INVALID;
+  if (batch < 1 || N < 1) return TV_ERR_INVALID;
+  if (N > 1024 || batch > 0x7fffffff) return TV_ERR_UNSUPPORTED;
+  return device_status(
+      tvk::launch_ancestors(parent, n_nodes, ctx_len, batch, N, depth, pos, anc_mask, stream));
+}
+
+// ---------------------------------------------------------------------------
+size_t tv_tree_attention_workspace(int batch, int N, int Hq, int Hkv, int D, int max_ctx,
+                                   int splits) {
+  if (!attn_args_ok(batch, N, Hq, Hkv, D, max_ctx, splits)) return 0;
+  return tvk::attention_plan(batch, N, Hq, Hkv, D, max_ctx, splits).workspace;
+}
+
+tv_status tv_tree_attention_verify(const void* q, const void* k_cache, const void* v_cache,
+                                   tv_dtype dt, const int32_t* ctx_len,
+                                   const uint64_t* anc_mask, const int32_t* n_nodes,
+                                   int batch, int N, int Hq, int Hkv, int D, int cap,
+                                   int max_ctx, float scale, int splits, void* out,
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !ctx_len || !anc_mask || !n_nodes || !out)
+    return TV_ERR_INVALID;
+  if (dt != TV_F32 && dt != TV_BF16) return TV_ERR_INVALID;
+  if (batch < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_ctx < 0 || splits < 0 ||
+      !finite_pos(scale))
+    return TV_ERR_INVALID;
+  if ((int64_t)max_ctx + N > (int64_t)cap) return TV_ERR_INVALID;
+  if (!attn_args_ok(batch, N, Hq, Hkv, D, max_ctx, splits)) return TV_ERR_UNSUPPORTED;
+  if ((int64_t)batch * Hkv > kMaxGridY) return TV_ERR_UNSUPPORTED;
+  const tvk::AttnPlan p = tvk::attention_plan(batch, N, Hq, Hkv, D, max_ctx, splits);
+  if (dt == TV_BF16 && (!workspace || workspace_bytes < p.workspace)) return TV_ERR_WORKSPACE;
+  return device_status(tvk::launch_attention(p, q, k_cache, v_cache, dt == TV_BF16, ctx_len,
+                                             anc_mask, n_nodes, batch, N, Hq, Hkv, D, cap,
+                                             max_ctx, scale, out, lse, workspace, stream));
+}
+
+// ---------------------------------------------------------------------------
+size_t tv_tree_accept_workspace(int batch, int N, int K, int V, tv_accept_mode mode,
+                                tv_proposal proposal) {
+  if (!accept_args_ok(batch, N, V, 1)) return 0;
+  const bool sampled = mode == TV_SAMPLED;
+  const bool draft = sampled && proposal == TV_PROPOSAL_DRAFT;
+  if (draft && K < 1) return 0;
+  return tvk::accept_plan(batch, N, K, V, sampled, draft).workspace;
+}
+
+tv_status tv_tree_accept(const void* target_logits, const void* draft_logits, tv_dtype dt,
+                         int batch, int N, int K, int V, const int32_t* parent,
+                         const int32_t* token, const int32_t* depth, const int32_t* n_nodes,
+                         tv_accept_mode mode, float temperature, tv_proposal proposal,
+                         uint64_t seed, uint64_t round, int max_depth, int32_t* accept_len,
+                         int32_t* accepted_nodes, int32_t* out_tokens, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (!target_logits || !parent || !token || !depth || !n_nodes || !accept_len ||
+      !accepted_nodes || !out_tokens)
+    return TV_ERR_INVALID;
+  if (dt != TV_F32 && dt != TV_BF16) return TV_ERR_INVALID;
+  if (mode != TV_GREEDY && mode != TV_SAMPLED) return TV_ERR_INVALID;
+  if (proposal != TV_PROPOSAL_POINT_MASS && proposal != TV_PROPOSAL_DRAFT)
+    return TV_ERR_INVALID;
+  const bool sampled = mode == TV_SAMPLED;
+  const bool draft = sampled && proposal == TV_PROPOSAL_DRAFT;
+  if (sampled && !finite_pos(temperature)) return TV_ERR_INVALID;
+  if (draft && (!draft_logits || K < 1)) return TV_ERR_INVALID;
+  if (batch < 1 || N < 1 || V < 1 || max_depth < 1) return TV_ERR_INVALID;
+  if (!accept_args_ok(batch, N, V, max_depth)) return TV_ERR_UNSUPPORTED;
+  const tvk::AcceptPlan p = tvk::accept_plan(batch, N, K, V, sampled, draft);
+  if (p.rows > kMaxGridY) return TV_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < p.workspace) return TV_ERR_WORKSPACE;
+  const float inv_t = sampled ? 1.0f / temperature : 1.0f;
+  return device_status(tvk::launch_accept(p, target_logits, draft ? draft_logits : nullptr,
+                                          dt == TV_BF16, batch, N, K, V, parent, token, depth,
+                                          n_nodes, sampled, inv_t, draft, seed, round,
+                                          max_depth, accept_len, accepted_nodes, out_tokens,
+                                          workspace, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,329 @@
+// tv_device.h -- device-side building blocks shared by the gfx950 kernels of
+// libtreeverify: the fixed-point softmax weight, Philox4x64-10, 64-lane
+// wavefront helpers and a block-wide top-k.
+//
+// Every translation unit that uses exp_spec / weight / Philox for an integer
+// decision is compiled with -ffp-contract=off: each float operation below is
+// one IEEE operation in the order written.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tvk {
+
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------------------
+// e^x for fp32 x <= 0 (0 below -32).  Cody-Waite reduction x = n ln2 + r with
+// n = rint(x * log2e) and ln2 split into a high part with 12 significand
+// bits (0x3f317000) and the fp32 rounding of the remainder (0x3805fdf4);
+// e^r from its Taylor series to degree 7 (coefficients fp32(1/i!)) by Horner
+// with fused multiply-adds; the result is scaled by 2^n exactly.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float exp_spec(float x) {
+  if (!(x >= -32.0f)) return 0.0f;
+  const float kLog2e = __builtin_bit_cast(float, 0x3fb8aa3bu);
+  const float kLn2Hi = __builtin_bit_cast(float, 0x3f317000u);
+  const float kLn2Lo = __builtin_bit_cast(float, 0x3805fdf4u);
+  const float c7 = __builtin_bit_cast(float, 0x39500d01u);
+  const float c6 = __builtin_bit_cast(float, 0x3ab60b61u);
+  const float c5 = __builtin_bit_cast(float, 0x3c088889u);
+  const float c4 = __builtin_bit_cast(float, 0x3d2aaaabu);
+  const float c3 = __builtin_bit_cast(float, 0x3e2aaaabu);
+  const float c2 = 0.5f;
+  float t = x * kLog2e;
+  float n = __builtin_rintf(t);
+  float r = __builtin_fmaf(-n, kLn2Hi, x);
+  r = __builtin_fmaf(-n, kLn2Lo, r);
+  float p = c7;
+  p = __builtin_fmaf(p, r, c6);
+  p = __builtin_fmaf(p, r, c5);
+  p = __builtin_fmaf(p, r, c4);
+  p = __builtin_fmaf(p, r, c3);
+  p = __builtin_fmaf(p, r, c2);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  return __builtin_ldexpf(p, (int)n);
+}
+
+// Fixed-point weight of logit l in a row with maximum m at inverse
+// temperature inv_t: rint(exp_spec(fl32(fl32(l - m) * inv_t)) * 2^44).
+__device__ __forceinline__ uint64_t weight(float l, float m, float inv_t) {
+  float d = l - m;
+  float x = d * inv_t;
+  float e = exp_spec(x);
+  float s = e * 17592186044416.0f;  // 2^44
+  return (uint64_t)__builtin_rintf(s);
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x64-10 (Salmon et al., SC'11).
+// ---------------------------------------------------------------------------
+struct u64x4 {
+  uint64_t v[4];
+};
+
+__device__ __forceinline__ u64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2,
+                                               uint64_t c3, uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int rnd = 0; rnd < 10; ++rnd) {
+    if (rnd > 0) {
+      k0 += W0;
+      k1 += W1;
+    }
+    uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+    uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    uint64_t n0 = hi1 ^ c1 ^ k0;
+    uint64_t n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  u64x4 r;
+  r.v[0] = c0;
+  r.v[1] = c1;
+  r.v[2] = c2;
+  r.v[3] = c3;
+  return r;
+}
+
+constexpr uint64_t kResidualSlot = 0xFFFFFFFFull;
+
+// ---------------------------------------------------------------------------
+// element loads
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+};
+template <>
+struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p, int64_t i) {
+    return bf16_to_f32(p[i]);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// wavefront helpers (wave64)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ int readlane_i(int v, int l) {
+  return __builtin_amdgcn_readlane(v, l);
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  return __builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, v), l));
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+  uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int d) {
+  uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)v, d);
+  uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(v >> 32), d);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 1; m < WAVE; m <<= 1) v += shfl_xor_u64(v, m);
+  return v;
+}
+// inclusive prefix sum over lanes
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    uint64_t o = shfl_up_u64(v, d);
+    if (l >= d) v += o;
+  }
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan_i(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    int o = __shfl_up(v, d);
+    if (l >= d) v += o;
+  }
+  return v;
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int m = 1; m < WAVE; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// (value, id) order used by top-k and argmax: larger value first, then the
+// smaller id.  Ids of padding entries are >= the vocabulary and distinct.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool vi_better(float av, int ai, float bv, int bi) {
+  return av > bv || (av == bv && ai < bi);
+}
+
+// Argmax over a wave of (value, id) pairs in the order above.
+__device__ __forceinline__ void wave_argmax(float& v, int& id) {
+#pragma unroll
+  for (int m = 1; m < WAVE; m <<= 1) {
+    float ov = __shfl_xor(v, m);
+    int oi = __shfl_xor(id, m);
+    if (vi_better(ov, oi, v, id)) {
+      v = ov;
+      id = oi;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block-wide top-k (k <= 64) of E (value, id) items per thread, in the order
+// above.  Result: out_v / out_i [k] in LDS-or-global memory, best first.
+//
+// Each wave takes the k-th best of its 64 per-thread maxima as a threshold
+// (every item of the wave's top-k is at least as good, so the survivors
+// contain the block's top-k), keeps the items at least as good as its
+// threshold, and the survivors are ranked by counting.  If a wave keeps more
+// than kCap items (heavy ties) the block falls back to k rounds of argmax.
+// Requires blockDim.x == NT, a multiple of 64, and the scratch below.
+// ---------------------------------------------------------------------------
+template <int NT>
+struct TopkScratch {
+  static constexpr int kWaves = NT / WAVE;
+  static constexpr int kCap = 256;
+  float sv[kWaves * kCap];
+  int si[kWaves * kCap];
+  int wcount[kWaves];
+  int overflow;
+  float rv[kWaves];
+  int ri[kWaves];
+};
+
+template <int NT, int E>
+__device__ void block_topk(float (&val)[E], int (&id)[E], int k, TopkScratch<NT>& sc,
+                           float* out_v, int* out_i) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
+  constexpr int kCap = TopkScratch<NT>::kCap;
+  if (tid == 0) sc.overflow = 0;
+  // per-thread best
+  float bv = val[0];
+  int bi = id[0];
+#pragma unroll
+  for (int e = 1; e < E; ++e)
+    if (vi_better(val[e], id[e], bv, bi)) {
+      bv = val[e];
+      bi = id[e];
+    }
+  // rank of this lane's best among the wave's 64 (all pairs are distinct)
+  int rank = 0;
+  for (int j = 0; j < WAVE; ++j) {
+    float ov = readlane_f(bv, j);
+    int oi = readlane_i(bi, j);
+    rank += vi_better(ov, oi, bv, bi) ? 1 : 0;
+  }
+  uint64_t hit = __ballot(rank == k - 1);
+  int tl = __ffsll((unsigned long long)hit) - 1;
+  float tv = readlane_f(bv, tl);
+  int ti = readlane_i(bi, tl);
+  // survivors: items at least as good as the threshold
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) cnt += vi_better(tv, ti, val[e], id[e]) ? 0 : 1;
+  int incl = wave_incl_scan_i(cnt);
+  int total = readlane_i(incl, WAVE - 1);
+  __syncthreads();  // overflow flag initialised
+  if (total > kCap) {
+    if (lane == 0) sc.overflow = 1;
+  } else {
+    int off = incl - cnt;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (!vi_better(tv, ti, val[e], id[e])) {
+        sc.sv[wave * kCap + off] = val[e];
+        sc.si[wave * kCap + off] = id[e];
+        ++off;
+      }
+  }
+  if (lane == 0) sc.wcount[wave] = total;
+  __syncthreads();
+  if (!sc.overflow) {
+    // rank survivors by counting; survivors live in per-wave segments
+    int nsurv = 0;
+    for (int w = 0; w < NT / WAVE; ++w) nsurv += sc.wcount[w];
+    for (int t = tid; t < nsurv; t += NT) {
+      int w = 0, loc = t;
+      while (loc >= sc.wcount[w]) {
+        loc -= sc.wcount[w];
+        ++w;
+      }
+      float xv = sc.sv[w * kCap + loc];
+      int xi = sc.si[w * kCap + loc];
+      int r = 0;
+      for (int w2 = 0; w2 < NT / WAVE; ++w2)
+        for (int j = 0; j < sc.wcount[w2]; ++j)
+          r += vi_better(sc.sv[w2 * kCap + j], sc.si[w2 * kCap + j], xv, xi) ? 1 : 0;
+      if (r < k) {
+        out_v[r] = xv;
+        out_i[r] = xi;
+      }
+    }
+    __syncthreads();
+    return;
+  }
+  // fallback: k rounds of block argmax, removing the winner each round
+  bool taken[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) taken[e] = false;
+  for (int r = 0; r < k; ++r) {
+    float mv = -__builtin_inff();
+    int mi = 0x7fffffff;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (!taken[e] && vi_better(val[e], id[e], mv, mi)) {
+        mv = val[e];
+        mi = id[e];
+      }
+    wave_argmax(mv, mi);
+    if (lane == 0) {
+      sc.rv[wave] = mv;
+      sc.ri[wave] = mi;
+    }
+    __syncthreads();
+    float gv = sc.rv[0];
+    int gi = sc.ri[0];
+    for (int w = 1; w < NT / WAVE; ++w)
+      if (vi_better(sc.rv[w], sc.ri[w], gv, gi)) {
+        gv = sc.rv[w];
+        gi = sc.ri[w];
+      }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (id[e] == gi && val[e] == gv) taken[e] = true;
+    if (tid == 0) {
+      out_v[r] = gv;
+      out_i[r] = gi;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace tvk

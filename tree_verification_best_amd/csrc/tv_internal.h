@@ -1,0 +1,76 @@
+// tv_internal.h -- host-side plans and kernel launchers of libtreeverify
+// (shared between the API translation unit and the kernel files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <cstddef>
+
+#define TV_MAX_TOPK_ 64
+
+namespace tvk {
+
+// ---- build ----
+constexpr int kBuildChunk = 8192;  // tokens per block in the draft-row passes
+constexpr int kFinalizeE = 8;      // per-thread items when merging chunk candidates
+
+struct BuildPlan {
+  int chunk, C;
+  int64_t rows;
+  int P, Q2;  // LDS sort buffer (candidates of one depth) and merge buffer sizes
+  size_t select_lds;
+  size_t off_cval, off_cid, off_cz, off_ftok, off_fq;
+  size_t workspace;
+};
+
+BuildPlan build_plan(int batch, int K, int V, int topk, int budget);
+hipError_t launch_build(const BuildPlan& p, const void* draft, bool bf16, int batch, int K,
+                        int V, int topk, int budget, float inv_t, const int* root_token,
+                        const int* ctx_len, int* parent, int* token, int* depth, int* pos,
+                        double* score, uint64_t* anc, int* n_nodes, void* ws,
+                        hipStream_t stream);
+hipError_t launch_ancestors(const int* parent, const int* n_nodes, const int* ctx_len,
+                            int batch, int N, int* depth, int* pos, uint64_t* anc,
+                            hipStream_t stream);
+
+// ---- attention ----
+struct AttnPlan {
+  int rows_per_kv;  // G * N
+  int row_blocks;   // ceil(rows_per_kv / 32)
+  int waves;        // waves per workgroup
+  int mtiles;       // workgroups along the rows of one KV head
+  int splits;       // context splits (the tree keys get one more)
+  int keys_per_split;
+  size_t off_o, off_ml;
+  size_t workspace;
+};
+
+AttnPlan attention_plan(int batch, int N, int Hq, int Hkv, int D, int max_ctx, int splits);
+hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, const void* v,
+                            bool bf16, const int* ctx_len, const uint64_t* anc,
+                            const int* n_nodes, int batch, int N, int Hq, int Hkv, int D,
+                            int cap, int max_ctx, float scale, void* out, float* lse,
+                            void* ws, hipStream_t stream);
+
+// ---- accept ----
+constexpr int kAcceptChunk = 4096;  // tokens per block in the logits passes
+
+struct AcceptPlan {
+  int chunk, C;
+  int64_t rows;  // batch * N target rows (+ batch * K draft rows in DRAFT mode)
+  bool draft_rows;
+  size_t off_cmax, off_carg, off_cz;
+  size_t workspace;
+};
+
+AcceptPlan accept_plan(int batch, int N, int K, int V, bool sampled, bool draft);
+hipError_t launch_accept(const AcceptPlan& p, const void* target, const void* draft,
+                         bool bf16, int batch, int N, int K, int V, const int* parent,
+                         const int* token, const int* depth, const int* n_nodes, bool sampled,
+                         float inv_t, bool draft_proposal, uint64_t seed, uint64_t round,
+                         int max_depth, int* accept_len, int* accepted_nodes, int* out_tokens,
+                         void* ws, hipStream_t stream);
+
+}  // namespace tvk
