@@ -1,0 +1,323 @@
+"""Benchmark: one tree-verification round per step on one MI355X.
+
+A step is the whole round on one batch of synthetic input already resident in
+HBM: tv_tree_build -> tv_tree_attention_verify (one layer) -> tv_tree_accept.
+The default workload is the 4B-class GQA layer (32 query / 8 KV heads, head
+dim 128, bf16, context 4096, K = 16 draft positions, top-8, budget 64,
+vocabulary 151936, sampled acceptance at T = 1).  Inputs rotate over enough
+independent sets (>= 1 GiB) that every step reads HBM, not the 256 MB
+Infinity Cache.
+
+Prints ONE JSON line (rank 0).  `value` = tree node x query-head rows
+verified per second (rounds/s x N x Hq).  `roofline` is for the kernel(s) of
+the dominant call, from HIP events recorded around every call on the stream
+the call runs on.  `cpu_baseline` times the CPU oracle on a bounded sample
+of the same workload.
+
+    python bench.py [--gpus 1] [--steps 500] [--warmup 50] [--workload 4b]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="4b", choices=["4b", "8b", "long", "batched", "tiny"])
+    ap.add_argument("--temperature", type=float, default=1.0, help="0 = greedy")
+    ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--graph", action="store_true", help="replay each round from a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(c, b, N, Lsum, build):
+    """Each input read once, each output written once, at its dtype."""
+    V, K, Hq, Hkv, D = c["V"], c["K"], c["Hq"], c["Hkv"], c["D"]
+    el = 2 if c["dtype"] == "bf16" else 4
+    W = (N + 63) // 64
+    out = {}
+    out["build"] = (b * K * V * 4 + b * N * (4 * 4 + 8 + 8 * W)) if build else 0
+    kv = 2 * Hkv * D * el * (Lsum + b * N)            # context rows + tree rows, K and V
+    qo = 2 * b * N * Hq * D * el + b * N * Hq * 4     # Q in, O out, lse out
+    out["attention"] = kv + qo + b * N * 8 * W
+    out["accept"] = b * N * V * 4 + b * N * 12
+    return out
+
+
+def attention_flops(c, n_nodes, depths, ctx):
+    """4 Hq D sum_i (L + depth_i + 1): unmasked score entries x 2 matmuls x 2."""
+    tot = 0
+    for s in range(len(n_nodes)):
+        n = int(n_nodes[s])
+        tot += sum(int(ctx[s]) + int(depths[s][i]) + 1 for i in range(n))
+    return 4 * c["Hq"] * c["D"] * tot
+
+
+def cpu_baseline(c, sets0, seconds):
+    """The oracle, untuned, on the same first input set: whole rounds until
+    `seconds` of CPU time are spent (at least one)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    draft, target, q, k, v, roots, ctx = sets0
+    b, N = target.shape[0], target.shape[1]
+    mode = oracle.GREEDY if c["_T"] == 0 else oracle.SAMPLED
+    rounds, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            if c["build"]:
+                tr = oracle.tree_build(draft, c["k"], c["B"], roots, ctx)
+                parent, token, depth, anc, nn = (tr["parent"], tr["token"], tr["depth"],
+                                                 tr["anc"], tr["n_nodes"])
+            else:
+                parent, token, depth, anc, nn = c["_tree"]
+            oracle.tree_attention(q, k, v, ctx, anc, nn)
+            oracle.tree_accept(target, parent, token, depth, nn, mode=mode,
+                               temperature=max(c["_T"], 1e-3), seed=1234, round=rounds,
+                               max_depth=c["K"])
+            rounds += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    dt = time.perf_counter() - t0
+    return rounds, dt
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the path has no multi-GPU mode (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import tree_verification_best_amd as tv
+    import workloads
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    c = dict(workloads.CONFIGS[args.workload])
+    c["_T"] = args.temperature
+    b, N, V, K = c["batch"], c["B"] + 1, c["V"], c["K"]
+    bf = c["dtype"] == "bf16"
+    tdt = torch.bfloat16 if bf else torch.float32
+
+    # ---- input sets ------------------------------------------------------
+    def make_set(salt):
+        draft, target = workloads.logits(c, b, N, salt=salt)
+        roots = workloads.root_tokens(c, b, salt=salt)
+        ctx = workloads.context_lengths(c, b, salt=0)
+        cap = int(ctx.max()) + N
+        q, k, v = workloads.qkv(c, b, N, cap, salt=salt)
+        return draft, target, q, k, v, roots, ctx
+
+    first = make_set(0)
+    per_set = sum(a.nbytes for a in first[:2]) + sum(a.nbytes // (2 if bf else 1)
+                                                      for a in first[2:5])
+    nsets = max(2, math.ceil(args.rotate_gib * 2 ** 30 / per_set))
+    tree_in = None
+    if not c["build"]:
+        parent, token, depth = workloads.random_trees(c, b, N, max_depth=K,
+                                                      max_children=c.get("max_children", 4))
+        nn = np.full(b, N, np.int32)
+        import oracle  # only to lay out the fixed random trees' ancestor rows for the CPU leg
+        anc = np.stack([oracle.ancestors(parent[s])[0] for s in range(b)])
+        c["_tree"] = (parent, token, depth, anc, nn)
+        first = (first[0], workloads.plant(first[1], parent, token, nn, 9.0)) + first[2:]
+        tree_in = [torch.from_numpy(a).to(dev) for a in (parent, token, nn)]
+
+    def to_dev(s):
+        draft, target, q, k, v, roots, ctx = s
+        # logits stay fp32 (4 bytes per element); Q/K/V use the layer's dtype
+        return dict(draft=torch.from_numpy(draft).to(dev), target=torch.from_numpy(target).to(dev),
+                    q=torch.from_numpy(q).to(dev, tdt), k=torch.from_numpy(k).to(dev, tdt),
+                    v=torch.from_numpy(v).to(dev, tdt), roots=torch.from_numpy(roots).to(dev),
+                    ctx=torch.from_numpy(ctx).to(dev))
+
+    sets = [to_dev(first)]
+    for i in range(1, nsets):
+        s = make_set(i)
+        if not c["build"]:
+            s = (s[0], workloads.plant(s[1], *c["_tree"][:2], c["_tree"][4], 9.0)) + s[2:]
+        sets.append(to_dev(s))
+    ctx0 = first[6]
+    max_ctx = int(ctx0.max())
+
+    # ---- preallocated outputs and workspaces -----------------------------
+    W = (N + 63) // 64
+    i32 = dict(dtype=torch.int32, device=dev)
+    tree = dict(parent=torch.empty((b, N), **i32), token=torch.empty((b, N), **i32),
+                depth=torch.empty((b, N), **i32), pos=torch.empty((b, N), **i32),
+                score=torch.empty((b, N), dtype=torch.float64, device=dev),
+                anc=torch.empty((b, N, W), dtype=torch.int64, device=dev),
+                n_nodes=torch.empty((b,), **i32))
+    sampled = args.temperature > 0
+    mode = tv.TV_SAMPLED if sampled else tv.TV_GREEDY
+    ws_b = torch.empty(max(tv.tree_build_workspace(b, K, V, c["k"], c["B"]), 1), dtype=torch.uint8, device=dev) if c["build"] else None
+    ws_a = torch.empty(tv.attention_workspace(b, N, c["Hq"], c["Hkv"], c["D"], max_ctx), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(tv.accept_workspace(b, N, K, V, mode), dtype=torch.uint8, device=dev)
+    attn_out = torch.empty((b, N, c["Hq"], c["D"]), dtype=tdt, device=dev)
+    lse = torch.empty((b, N, c["Hq"]), dtype=torch.float32, device=dev)
+    acc = dict(accept_len=torch.empty((b,), **i32), accepted_nodes=torch.empty((b, K + 1), **i32),
+               out_tokens=torch.empty((b, K + 1), **i32))
+    if not c["build"]:
+        tree["parent"].copy_(tree_in[0])
+        tree["token"].copy_(tree_in[1])
+        tree["n_nodes"].copy_(tree_in[2])
+
+    stream = torch.cuda.current_stream(dev)
+
+    def round_(step, ev=None):
+        s = sets[step % nsets]
+        if ev is not None:
+            ev[0].record(stream)
+        if c["build"]:
+            tv.tv_tree_build(s["draft"], c["k"], c["B"], s["roots"], s["ctx"], workspace=ws_b, out=tree)
+        else:
+            tv.tv_tree_ancestors(tree["parent"], tree["n_nodes"], s["ctx"],
+                                 out=dict(depth=tree["depth"], pos=tree["pos"], anc=tree["anc"]))
+        if ev is not None:
+            ev[1].record(stream)
+        tv.tv_tree_attention_verify(s["q"], s["k"], s["v"], s["ctx"], tree["anc"], tree["n_nodes"],
+                                    max_ctx, workspace=ws_a, out=attn_out, lse=lse)
+        if ev is not None:
+            ev[2].record(stream)
+        tv.tv_tree_accept(s["target"], tree["parent"], tree["token"], tree["depth"], tree["n_nodes"],
+                          mode=mode, temperature=max(args.temperature, 1e-3), seed=1234, round=step,
+                          max_depth=K, workspace=ws_c, out=acc)
+        if ev is not None:
+            ev[3].record(stream)
+
+    graphs = None
+    if args.graph:
+        # one graph per input set; replays alternate sets like the eager loop
+        graphs = []
+        for i in range(nsets):
+            round_(i)
+        torch.cuda.synchronize()
+        for i in range(nsets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                round_(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def step_fn(i, ev=None):
+        if graphs is not None:
+            if ev is not None:
+                ev[0].record(stream)
+            graphs[i % nsets].replay()
+            if ev is not None:
+                for e in ev[1:]:
+                    e.record(stream)
+        else:
+            round_(i, ev)
+
+    for i in range(args.warmup):
+        step_fn(i)
+    torch.cuda.synchronize()
+
+    # per-call events on the stream the calls run on
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step_fn(args.warmup + i, evs[i] if graphs is None else None)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    calls = {}
+    if graphs is None:
+        for name, (a, z) in (("build", (0, 1)), ("attention", (1, 2)), ("accept", (2, 3))):
+            calls[name] = sum(evs[i][a].elapsed_time(evs[i][z]) for i in range(args.steps)) / args.steps
+
+    # ---- accounting ------------------------------------------------------
+    nn_h = tree["n_nodes"].cpu().numpy()
+    dep_h = tree["depth"].cpu().numpy()
+    Lsum = int(ctx0.sum())
+    abytes = algorithmic_bytes(c, b, N, Lsum, c["build"])
+    aflops = attention_flops(c, nn_h, dep_h, ctx0)
+    rows = b * N * c["Hq"]
+    rounds_per_s = 1e3 / ms_per_step
+    value = rounds_per_s * rows
+    roof = None
+    per_call = {}
+    for name, ms in calls.items():
+        gbs = abytes[name] / (ms * 1e-3) / 1e9
+        per_call[name] = dict(ms=round(ms, 5), algorithmic_MB=round(abytes[name] / 1e6, 3),
+                              GBps=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+    if "attention" in calls:
+        tf = aflops / (calls["attention"] * 1e-3) / 1e12
+        per_call["attention"]["TFLOPs"] = round(tf, 2)
+        per_call["attention"]["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+    if calls:
+        dom = max(calls, key=lambda k: calls[k])
+        kernels = {"build": "k_chunk_topk+k_chunk_z+k_finalize+k_select",
+                   "attention": "k_attn_partial+k_attn_combine",
+                   "accept": "k_rowmax+k_rowz+k_walk"}
+        gbs = abytes[dom] / (calls[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "call": "tv_tree_" + dom,
+                "kernels": kernels[dom], "ms": round(calls[dom], 5),
+                "algorithmic_bytes": abytes[dom]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        r, dt = cpu_baseline(c, first, args.cpu_seconds)
+        cpu = {"value": round(r / dt * rows, 1), "unit": "node-heads/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{r} whole round(s) of the {args.workload} workload (input set 0), "
+                         f"{dt:.1f} s, single thread (BLAS limited to 1)"}
+
+    res = {
+        "metric": "verify rounds/s as tree node x query-head rows verified per second",
+        "value": round(value, 1),
+        "unit": "node-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 attention / f32 logits / u64 weights",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {c['Hq']}q/{c['Hkv']}kv heads, D={c['D']}, "
+                               f"{c['dtype']}, batch {b}, ctx {c['L']}, K={K}, top-{c['k']}, "
+                               f"B={c['B']}, V={V}, T={args.temperature}",
+                   "rounds_per_s": round(rounds_per_s, 2), "nodes": N,
+                   "input_sets": nsets, "graph": bool(args.graph),
+                   "round_algorithmic_MB": round(sum(abytes.values()) / 1e6, 2),
+                   "attention_GFLOP": round(aflops / 1e9, 3),
+                   "mean_accept_len": float(acc["accept_len"].float().mean().item()),
+                   "per_call": per_call, "wall_s": round(wall, 3)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

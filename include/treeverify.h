@@ -155,14 +155,18 @@ tv_status tv_tree_ancestors(const int32_t *parent, const int32_t *n_nodes,
  *   ctx_len  int32 [batch], 0 <= L_b <= max_ctx (precondition)
  *   anc_mask uint64 [batch][N][ceil(N/64)] as written by tv_tree_build
  *   n_nodes  int32 [batch], 1 <= n_nodes[b] <= N (precondition)
- *   out      [batch][N][Hq][D]       dtype dt
+ *   out      [batch][N][Hq][D]       dtype out_dt: TV_F32 (the fp32 result of
+ *            the accumulation) or, for bf16 inputs, TV_BF16 (rounded to
+ *            nearest even; fp32 inputs need TV_F32)
  *   lse      float [batch][N][Hq], may be NULL
  *   splits   number of context splits (0 = automatic); partial results are
  *            merged with their log-sum-exp weights.
  *   Rows past n_nodes: out 0, lse -inf.
  * Limits: D in {64, 128}; Hq % Hkv == 0; N <= 1024; max_ctx + N <= cap.
  * bf16: bf16 products on the matrix cores with fp32 accumulation and an
- * fp32 online softmax.  f32: fp32 throughout (vector ALU).
+ * fp32 online softmax; the softmax weights enter the second product
+ * rounded to bf16 while the normaliser sums them in fp32.  f32: fp32
+ * throughout (vector ALU).
  * ------------------------------------------------------------------------ */
 size_t tv_tree_attention_workspace(int batch, int N, int Hq, int Hkv, int D, int max_ctx,
                                    int splits);
@@ -171,8 +175,8 @@ tv_status tv_tree_attention_verify(const void *q, const void *k_cache, const voi
                                    const uint64_t *anc_mask, const int32_t *n_nodes,
                                    int batch, int N, int Hq, int Hkv, int D, int cap,
                                    int max_ctx, float scale, int splits, void *out,
-                                   float *lse, void *workspace, size_t workspace_bytes,
-                                   hipStream_t stream);
+                                   tv_dtype out_dt, float *lse, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * tv_tree_accept -- the acceptance walk over one tree per sequence.

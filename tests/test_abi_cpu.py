@@ -88,14 +88,14 @@ def test_build_rejects(kw, status):
 
 def _attn(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, dt=1, ctx=FAKE, anc=FAKE, n=FAKE, batch=1, N=17, Hq=4,
-             Hkv=2, D=128, cap=200, max_ctx=128, scale=0.1, splits=0, out=FAKE, lse=None,
-             ws=FAKE, wsb=1 << 30)
+             Hkv=2, D=128, cap=200, max_ctx=128, scale=0.1, splits=0, out=FAKE, odt=0,
+             lse=None, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return tv.lib().tv_tree_attention_verify(a["q"], a["k"], a["v"], a["dt"], a["ctx"],
                                              a["anc"], a["n"], a["batch"], a["N"], a["Hq"],
                                              a["Hkv"], a["D"], a["cap"], a["max_ctx"],
-                                             a["scale"], a["splits"], a["out"], a["lse"],
-                                             a["ws"], a["wsb"], None)
+                                             a["scale"], a["splits"], a["out"], a["odt"],
+                                             a["lse"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -105,6 +105,8 @@ def _attn(**kw):
     (dict(cap=100), tv.TV_ERR_INVALID),          # max_ctx + N > cap
     (dict(scale=-1.0), tv.TV_ERR_INVALID),
     (dict(splits=-2), tv.TV_ERR_INVALID),
+    (dict(odt=7), tv.TV_ERR_INVALID),
+    (dict(dt=0, odt=1), tv.TV_ERR_UNSUPPORTED),        # fp32 inputs give fp32 output
     (dict(D=96), tv.TV_ERR_UNSUPPORTED),
     (dict(N=1025, cap=5000), tv.TV_ERR_UNSUPPORTED),
     (dict(ws=None), tv.TV_ERR_WORKSPACE),

@@ -117,3 +117,23 @@ def test_attention_full_size_sampled_rows(cfg):
         assert np.abs(d).max() <= 1e-2
         assert np.linalg.norm(d) / np.linalg.norm(ro) <= 2e-2
         assert np.abs(gl[s, i] - rl).max() <= 1e-2
+
+
+def test_attention_bf16_output_is_rounded_fp32():
+    """out_dtype=bf16 gives the fp32 result rounded to nearest even."""
+    r = np.random.default_rng(21)
+    b, N, Hq, Hkv, D, L = 2, 33, 8, 2, 128, 700
+    cap = L + N
+    q = bf16_dev(r.standard_normal((b, N, Hq, D)).astype(np.float32))
+    k = bf16_dev(r.standard_normal((b, Hkv, cap, D)).astype(np.float32))
+    v = bf16_dev(r.standard_normal((b, Hkv, cap, D)).astype(np.float32))
+    parent = np.concatenate([[-1], r.integers(0, np.arange(1, N))]).astype(np.int32)
+    anc = np.stack([oracle.ancestors(parent)[0]] * b)
+    args = (q, k, v, dev(np.array([L, 100], np.int32)), dev(anc.view(np.int64)),
+            dev(np.array([N, 20], np.int32)), L)
+    o32, l32 = tv.tv_tree_attention_verify(*args, splits=3)
+    o16, l16 = tv.tv_tree_attention_verify(*args, splits=3, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(l16, l32)

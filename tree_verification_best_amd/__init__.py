@@ -65,7 +65,7 @@ def _load():
     L.tv_tree_attention_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.tv_tree_attention_workspace.restype = sz
     L.tv_tree_attention_verify.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32,
-                                           i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
+                                           i32, i32, i32, f32, i32, vp, i32, vp, vp, sz, vp]
     L.tv_tree_attention_verify.restype = i32
     L.tv_tree_accept_workspace.argtypes = [i32, i32, i32, i32, i32, i32]
     L.tv_tree_accept_workspace.restype = sz
@@ -180,15 +180,18 @@ def attention_workspace(batch, N, Hq, Hkv, D, max_ctx, splits=0):
 
 def tv_tree_attention_verify(q, k_cache, v_cache, ctx_len, anc_mask, n_nodes, max_ctx,
                              scale=None, splits=0, want_lse=True, workspace=None, out=None,
-                             lse=None):
-    """q [b][N][Hq][D]; caches [b][Hkv][cap][D] -> (out [b][N][Hq][D], lse [b][N][Hq])."""
+                             lse=None, out_dtype=torch.float32):
+    """q [b][N][Hq][D]; caches [b][Hkv][cap][D] -> (out [b][N][Hq][D], lse [b][N][Hq]).
+
+    out is fp32 by default (the accumulated result); bf16 inputs may ask for
+    out_dtype=torch.bfloat16."""
     L = _load()
     b, N, Hq, D = q.shape
     Hkv, cap = k_cache.shape[1], k_cache.shape[2]
     dev = q.device
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=out_dtype, device=dev)
     if want_lse and lse is None:
         lse = torch.empty((b, N, Hq), dtype=torch.float32, device=dev)
     need = L.tv_tree_attention_workspace(b, N, Hq, Hkv, D, int(max_ctx), int(splits))
@@ -198,7 +201,7 @@ def tv_tree_attention_verify(q, k_cache, v_cache, ctx_len, anc_mask, n_nodes, ma
                                     _dev(ctx_len, "ctx_len", torch.int32),
                                     _dev(anc_mask, "anc_mask", torch.int64),
                                     _dev(n_nodes, "n_nodes", torch.int32), b, N, Hq, Hkv, D, cap,
-                                    int(max_ctx), scale, int(splits), _dev(out, "out", q.dtype),
+                                    int(max_ctx), scale, int(splits), _dev(out, "out"), _dt(out),
                                     _dev(lse, "lse", torch.float32) if lse is not None else None,
                                     ws.data_ptr(), wsb, _stream(dev))
     _check(st, "tv_tree_attention_verify")

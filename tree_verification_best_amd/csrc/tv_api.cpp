@@ -104,11 +104,13 @@ tv_status tv_tree_attention_verify(const void* q, const void* k_cache, const voi
                                    const uint64_t* anc_mask, const int32_t* n_nodes,
                                    int batch, int N, int Hq, int Hkv, int D, int cap,
                                    int max_ctx, float scale, int splits, void* out,
-                                   float* lse, void* workspace, size_t workspace_bytes,
-                                   hipStream_t stream) {
+                                   tv_dtype out_dt, float* lse, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !ctx_len || !anc_mask || !n_nodes || !out)
     return TV_ERR_INVALID;
   if (dt != TV_F32 && dt != TV_BF16) return TV_ERR_INVALID;
+  if (out_dt != TV_F32 && out_dt != TV_BF16) return TV_ERR_INVALID;
+  if (dt == TV_F32 && out_dt != TV_F32) return TV_ERR_UNSUPPORTED;
   if (batch < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_ctx < 0 || splits < 0 ||
       !finite_pos(scale))
     return TV_ERR_INVALID;
@@ -119,7 +121,8 @@ tv_status tv_tree_attention_verify(const void* q, const void* k_cache, const voi
   if (dt == TV_BF16 && (!workspace || workspace_bytes < p.workspace)) return TV_ERR_WORKSPACE;
   return device_status(tvk::launch_attention(p, q, k_cache, v_cache, dt == TV_BF16, ctx_len,
                                              anc_mask, n_nodes, batch, N, Hq, Hkv, D, cap,
-                                             max_ctx, scale, out, lse, workspace, stream));
+                                             max_ctx, scale, out, out_dt == TV_F32, lse,
+                                             workspace, stream));
 }
 
 // ---------------------------------------------------------------------------

@@ -31,32 +31,59 @@
 namespace tvk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kTile = 32;     // keys per tile
-constexpr int kAttnMaxWaves = 4;
+constexpr int kTileKeys = 64;  // keys staged per iteration (two 32-key MFMA sub-tiles)
+constexpr int kAttnWaves = 4;  // waves per workgroup, 32 query rows each
+constexpr int kAttnThreads = kAttnWaves * WAVE;
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   __bf16 h = (__bf16)x;
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations, not for its outstanding global loads (a prefetch stays in
+// flight across it).  __syncthreads() would also drain the global loads.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
+  return (a & 0xFFFFu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xFFFF0000u);
+}
+
+// Work items are (sequence x KV head, row tile, split) with the split fastest.
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
+// XCD w % 8), so workgroup w takes item (w % 8) * per + w / 8: every XCD gets
+// a contiguous range of items, i.e. all the splits of a few (KV head, row
+// tile) pairs, and the Q rows and K/V of a head stay in one XCD's L2.
 template <int D>
-__global__ __launch_bounds__(kAttnMaxWaves * WAVE) void k_attn_partial(
+__global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int* __restrict__ ctx_len,
     const uint64_t* __restrict__ anc, const int* __restrict__ n_nodes, int N, int Hq, int Hkv,
-    int cap, int S, int KS, float scale_log2, float* __restrict__ Opart,
+    int cap, int S, int KS, int MT, int items, float scale_log2, float* __restrict__ Opart,
     float* __restrict__ Mpart, float* __restrict__ Lpart, int batch) {
-  constexpr int KPAD = D + 8;       // K tile row stride (bf16)
-  constexpr int VPAD = kTile + 8;   // V^T tile row stride (bf16)
-  __shared__ __align__(16) uint16_t Ks[kTile * KPAD];
-  __shared__ __align__(16) uint16_t Vt[D * VPAD];
+  constexpr int KP = D + 8;          // K tile pitch (bf16): 16-byte reads spread over banks
+  constexpr int VP = kTileKeys + 4;  // V^T tile pitch (bf16)
+  constexpr int KCH = D / 8;         // 16-byte chunks per key row
+  constexpr int KLD = kTileKeys * KCH / kAttnThreads;       // K chunks per thread
+  constexpr int VGROUPS = (kTileKeys / 4) * KCH;            // (4 keys x 8 d) groups
+  __shared__ __align__(16) uint16_t Ks[kTileKeys * KP];
+  __shared__ __align__(16) uint16_t Vt[D * VP];
+  __shared__ uint64_t Aw[kAttnWaves * 32 * 16];  // ancestor rows (tree split)
 
-  const int split = blockIdx.x;
-  const int mt = blockIdx.y;
-  const int bg = blockIdx.z;
+  const int w = blockIdx.x;
+  const int per = (items + 7) / 8;
+  const int item = (w % 8) * per + w / 8;
+  if (item >= items) return;  // whole workgroup, before any barrier
+  const int split = item % (S + 1);
+  const int mt = (item / (S + 1)) % MT;
+  const int bg = item / ((S + 1) * MT);
   const int b = bg / Hkv, g = bg % Hkv;
   const int G = Hq / Hkv;
   // ctx_len <= max_ctx and max_ctx + N <= cap are preconditions; the clamp
@@ -65,15 +92,15 @@ __global__ __launch_bounds__(kAttnMaxWaves * WAVE) void k_attn_partial(
   const int n = min(n_nodes[b], N);
   const int W = (N + 63) / 64;
   const int tid = threadIdx.x;
-  const int nthreads = blockDim.x;
   const int wave = tid / WAVE, lane = tid % WAVE;
   const int half = lane >> 5, l32 = lane & 31;
-  const int nwaves = nthreads / WAVE;
 
-  const int row = (mt * nwaves + wave) * 32 + l32;
+  const int row0 = (mt * kAttnWaves + wave) * 32;
+  const int row = row0 + l32;
   const int node = row / G;
   const int h = g * G + row % G;
   const bool row_ok = node < n;
+  const bool wave_active = row0 < G * n;  // uniform per wave
 
   int k0, k1;
   if (split < S) {
@@ -84,7 +111,6 @@ __global__ __launch_bounds__(kAttnMaxWaves * WAVE) void k_attn_partial(
     k1 = L + n;
   }
 
-  // Q fragments: lane holds Q[row][c*16 + half*8 .. +8] for c < D/16
   bf16x8 qf[D / 16];
   {
     const uint16_t* qp = q + (((int64_t)b * N + (row_ok ? node : 0)) * Hq + h) * D;
@@ -95,8 +121,6 @@ __global__ __launch_bounds__(kAttnMaxWaves * WAVE) void k_attn_partial(
       qf[c] = __builtin_bit_cast(bf16x8, raw);
     }
   }
-  uint64_t anc_word_cache = 0;
-  int anc_word_idx = -1;
   const uint64_t* arow = anc + ((int64_t)b * N + (row_ok ? node : 0)) * W;
 
   f32x16 oacc[D / 32];
@@ -109,106 +133,164 @@ __global__ __launch_bounds__(kAttnMaxWaves * WAVE) void k_attn_partial(
 
   const uint16_t* kbase = kc + ((int64_t)b * Hkv + g) * (int64_t)cap * D;
   const uint16_t* vbase = vc + ((int64_t)b * Hkv + g) * (int64_t)cap * D;
-  constexpr int kChunksPerRow = D / 8;  // 16-byte pieces per key row
 
-  for (int kt = k0; kt < k1; kt += kTile) {
-    // ---- stage K (row-major) and V (transposed) for keys kt .. kt+31
-    for (int idx = tid; idx < kTile * kChunksPerRow; idx += nthreads) {
-      const int key = idx / kChunksPerRow;
-      const int col = (idx % kChunksPerRow) * 8;
-      uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
-      if (kt + key < k1) {
-        kr = *reinterpret_cast<const uint4*>(kbase + (int64_t)(kt + key) * D + col);
-        vr = *reinterpret_cast<const uint4*>(vbase + (int64_t)(kt + key) * D + col);
+  // register prefetch of one tile: K chunks and one (4 keys x 8 d) V group.
+  // Rows past the tile's end are clamped to the last valid row (always in
+  // bounds, no branch) and zeroed when staged.
+  uint4 kreg[KLD];
+  uint4 vreg[4];
+  auto fetch = [&](int kt) {
+    const int last = k1 - 1;
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int c = tid + i * kAttnThreads;
+      const int key = min(kt + c / KCH, last), col = (c % KCH) * 8;
+      kreg[i] = *reinterpret_cast<const uint4*>(kbase + (int64_t)key * D + col);
+    }
+    {
+      // every thread loads a V group (duplicates past VGROUPS are not
+      // staged) so the number of loads in flight is the same in every lane
+      const int gi = tid % VGROUPS;
+      const int kq = gi % (kTileKeys / 4), col = (gi / (kTileKeys / 4)) * 8;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = min(kt + 4 * kq + r, last);
+        vreg[r] = *reinterpret_cast<const uint4*>(vbase + (int64_t)key * D + col);
       }
-      *reinterpret_cast<uint4*>(&Ks[key * KPAD + col]) = kr;
-      const uint16_t* vv = reinterpret_cast<const uint16_t*>(&vr);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) Vt[(col + j) * VPAD + key] = vv[j];
     }
-    __syncthreads();
-
-    // ---- visibility of this tile's keys (the ancestor mask on the tree
-    // tile).  Computed before the matrix products so that their results are
-    // consumed in straight-line code: the MFMA result latency is covered by
-    // the wait states the compiler inserts inside one basic block.
-    uint32_t tmask = 0xFFFFFFFFu;
-    if (split == S) {
-      const int j0 = kt - L;  // multiple of 32
-      const int wi = j0 >> 6;
-      if (wi != anc_word_idx) {
-        anc_word_cache = row_ok ? arow[wi] : 0ull;
-        anc_word_idx = wi;
+  };
+  auto stage = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int c = tid + i * kAttnThreads;
+      const int key = c / KCH, col = (c % KCH) * 8;
+      *reinterpret_cast<uint4*>(&Ks[key * KP + col]) =
+          kt + key < k1 ? kreg[i] : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < VGROUPS) {
+      // lanes with consecutive tid hold consecutive 4-key groups of the same
+      // 8 d's: each 16-lane group writes one contiguous 128-byte V^T row
+      const int kq = tid % (kTileKeys / 4), col = (tid / (kTileKeys / 4)) * 8;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (kt + 4 * kq + r >= k1) vreg[r] = make_uint4(0, 0, 0, 0);
+      const uint32_t a[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
+      const uint32_t bq[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
+      const uint32_t cq[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
+      const uint32_t dq[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint2 ev = make_uint2(lo_halves(a[j], bq[j]), lo_halves(cq[j], dq[j]));
+        uint2 od = make_uint2(hi_halves(a[j], bq[j]), hi_halves(cq[j], dq[j]));
+        *reinterpret_cast<uint2*>(&Vt[(col + 2 * j) * VP + 4 * kq]) = ev;
+        *reinterpret_cast<uint2*>(&Vt[(col + 2 * j + 1) * VP + 4 * kq]) = od;
       }
-      tmask = (uint32_t)(anc_word_cache >> (j0 & 63));
     }
-    uint32_t vis = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kl = 8 * (i >> 2) + 4 * half + (i & 3);
-      const bool ok = row_ok && (kt + kl < k1) && ((tmask >> kl) & 1u);
-      vis |= (ok ? 1u : 0u) << i;
-    }
+  };
 
-    // ---- S^T = K Q^T  (32 keys x 32 rows)
-    f32x16 s;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const bf16x8 a =
-          __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Ks[l32 * KPAD + c * 16 + half * 8]));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s, 0, 0, 0);
-    }
+  // The tree split keeps each row's ancestor words in LDS, so the tile loop
+  // issues no global load other than the K/V prefetch: waiting for any other
+  // load would also wait for the prefetch (the vector memory counter retires
+  // in order).
+  uint64_t* aw = &Aw[(wave * 32 + l32) * 16];
+  if (split == S && half == 0)
+    for (int j = 0; j < W; ++j) aw[j] = row_ok ? arow[j] : 0ull;
 
-    // ---- online softmax (log2 domain)
-    float x[16];
-    float tmax = -__builtin_inff();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      x[i] = ((vis >> i) & 1u) ? s[i] * scale_log2 : -__builtin_inff();
-      tmax = fmaxf(tmax, x[i]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    float alpha, psum = 0.f;
-    float p[16];
-    if (m_new == -__builtin_inff()) {
-      alpha = 1.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) p[i] = 0.f;
-    } else {
-      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+  if (k0 < k1) fetch(k0);
+  for (int kt = k0; kt < k1; kt += kTileKeys) {
+    stage(kt);
+    lds_barrier();
+    fetch(min(kt + kTileKeys, k1 - 1));  // in flight during the products
+    const uint64_t aword = split == S ? aw[(kt - L) >> 6] : 0ull;  // kt - L: multiple of 64
+
+    if (wave_active) {
+      // visibility of the 64 keys, taken before the matrix products so that
+      // their results are consumed in straight-line code.  valid bit j =
+      // key kt + j exists for this row; the lane's 32 keys are nibbles
+      // 0, 2, ..., 14 of (valid >> 4 * half) (the S^T accumulator layout).
+      uint64_t valid = split == S ? (row_ok ? aword : 0ull) : (row_ok ? ~0ull : 0ull);
+      if (k1 - kt < 64) valid &= (1ull << (k1 - kt)) - 1ull;
+      uint64_t v = (valid >> (4 * half)) & 0x0F0F0F0F0F0F0F0Full;
+      v = (v | (v >> 4)) & 0x00FF00FF00FF00FFull;
+      v = (v | (v >> 8)) & 0x0000FFFF0000FFFFull;
+      v = (v | (v >> 16)) & 0x00000000FFFFFFFFull;
+      const uint32_t vis = (uint32_t)v;
+      const bool full = __ballot(vis != 0xFFFFFFFFu) == 0;  // wave-uniform
+
+      // S^T = K Q^T for the two 32-key sub-tiles
+      f32x16 s0, s1;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
+        s0[i] = 0.f;
+        s1[i] = 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        const bf16x8 a0 = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(&Ks[l32 * KP + c * 16 + half * 8]));
+        const bf16x8 a1 = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(&Ks[(32 + l32) * KP + c * 16 + half * 8]));
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[c], s1, 0, 0, 0);
+      }
+
+      // online softmax on raw scores (the scale is positive, so the max
+      // commutes with it): p = 2^((s - m) * scale * log2 e)
+      float x[32];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x[i] = s0[i];
+        x[16 + i] = s1[i];
+      }
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          x[i] = ((vis >> i) & 1u) ? x[i] : -__builtin_inff();
+      }
+      float tmax = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < 32; i += 2) tmax = fmaxf(tmax, fmaxf(x[i], x[i + 1]));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const bool grow = tmax > m_run;
+      if (__ballot(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - tmax) * scale_log2) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        m_run = grow ? tmax : m_run;
+      }
+      const float moff = m_run == -__builtin_inff() ? 0.f : -m_run * scale_log2;
+      float p[32];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], scale_log2, moff));
         psum += p[i];
       }
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      l_run += psum;
 
-    // ---- O^T += V^T P^T
+      // O^T += V^T P^T with P rounded to bf16 (the normaliser l keeps the
+      // fp32 weights)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      bf16x8 bp;
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) bp[j] = (__bf16)p[8 * t + j];
+        for (int t = 0; t < 2; ++t) {
+          bf16x8 bp;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const uint16_t* vrow = &Vt[(32 * db + l32) * VPAD + 4 * half + 16 * t];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-        const uint4 raw = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw), bp,
-                                                          oacc[db], 0, 0, 0);
-      }
+          for (int j = 0; j < 8; ++j) bp[j] = (__bf16)p[16 * ks + 8 * t + j];
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const uint16_t* vrow = &Vt[(32 * db + l32) * VP + 32 * ks + 16 * t + 4 * half];
+            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp, oacc[db], 0, 0, 0);
+          }
+        }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- partials.  The accumulators were last written by an MFMA in the
@@ -219,7 +301,7 @@ __global__ __launch_bounds__(kAttnMaxWaves * WAVE) void k_attn_partial(
   if (row_ok) {
     const int64_t pr = (((int64_t)split * batch + b) * N + node) * Hq + h;
     if (half == 0) {
-      Mpart[pr] = m_run;
+      Mpart[pr] = m_run * scale_log2;  // log2 domain (-inf stays -inf)
       Lpart[pr] = l_tot;
     }
     float* op = Opart + pr * D;
@@ -235,45 +317,85 @@ __global__ __launch_bounds__(kAttnMaxWaves * WAVE) void k_attn_partial(
   }
 }
 
-// Merge the S + 1 partials of every (sequence, node, head) row.
+// Merge the S + 1 partials of every query row of one (sequence, node):
+// weights 2^(m_s - M) / sum_s 2^(m_s - M) l_s, then a float4 sweep over
+// (head, d).
 template <typename OutT>
-__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ Opart,
+__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ Opart,
                                                      const float* __restrict__ Mpart,
                                                      const float* __restrict__ Lpart,
                                                      const int* __restrict__ n_nodes, int batch,
                                                      int N, int Hq, int D, int S1,
                                                      OutT* __restrict__ out,
                                                      float* __restrict__ lse) {
-  const int64_t rowid = blockIdx.x;  // (b * N + node) * Hq + h
-  const int b = (int)(rowid / ((int64_t)N * Hq));
-  const int node = (int)((rowid / Hq) % N);
-  const bool ok = node < min(n_nodes[b], N);
+  extern __shared__ float sw[];  // [S1][Hq] weights, then maxima and sums
+  const int bn = blockIdx.x;     // b * N + node
+  const int b = bn / N, node = bn % N;
+  const int64_t row0 = (int64_t)bn * Hq;
   const int64_t plane = (int64_t)batch * N * Hq;
-  float M = -__builtin_inff();
-  if (ok)
-    for (int s = 0; s < S1; ++s) M = fmaxf(M, Mpart[s * plane + rowid]);
-  float lsum = 0.f;
-  if (ok && M != -__builtin_inff())
-    for (int s = 0; s < S1; ++s) {
-      const float ms = Mpart[s * plane + rowid];
-      if (ms != -__builtin_inff()) lsum += exp2f(ms - M) * Lpart[s * plane + rowid];
+  const bool ok = node < min(n_nodes[b], N);
+  const int tid = threadIdx.x;
+  if (!ok) {
+    for (int e = tid; e < Hq * D; e += blockDim.x) {
+      if constexpr (sizeof(OutT) == 2)
+        out[row0 * D + e] = 0;
+      else
+        out[row0 * D + e] = 0.f;
     }
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float acc = 0.f;
-    if (ok && lsum > 0.f)
-      for (int s = 0; s < S1; ++s) {
-        const float ms = Mpart[s * plane + rowid];
-        if (ms != -__builtin_inff()) acc += exp2f(ms - M) * Opart[(s * plane + rowid) * D + d];
-      }
-    const float o = (ok && lsum > 0.f) ? acc / lsum : 0.f;
-    if constexpr (sizeof(OutT) == 2)
-      out[rowid * D + d] = f32_to_bf16_bits(o);
-    else
-      out[rowid * D + d] = o;
+    if (lse)
+      for (int hh = tid; hh < Hq; hh += blockDim.x) lse[row0 + hh] = -__builtin_inff();
+    return;
   }
-  if (lse && threadIdx.x == 0)
-    lse[rowid] = (ok && lsum > 0.f) ? (M + log2f(lsum)) * 0.69314718055994531f
-                                    : -__builtin_inff();
+  // one round trip for every (split, head) pair of this node
+  float* sm = sw + S1 * Hq;
+  float* sl = sm + S1 * Hq;
+  for (int e = tid; e < S1 * Hq; e += blockDim.x) {
+    const int s = e / Hq, hh = e % Hq;
+    sm[e] = Mpart[s * plane + row0 + hh];
+    sl[e] = Lpart[s * plane + row0 + hh];
+  }
+  __syncthreads();
+  for (int hh = tid; hh < Hq; hh += blockDim.x) {
+    float M = -__builtin_inff();
+    for (int s = 0; s < S1; ++s) M = fmaxf(M, sm[s * Hq + hh]);
+    float lsum = 0.f;
+    for (int s = 0; s < S1; ++s) {
+      const float ms = sm[s * Hq + hh];
+      const float wgt = ms == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+      sw[s * Hq + hh] = wgt;
+      lsum += wgt * sl[s * Hq + hh];
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    for (int s = 0; s < S1; ++s) sw[s * Hq + hh] *= inv;
+    if (lse) lse[row0 + hh] = lsum > 0.f ? (M + log2f(lsum)) * 0.69314718055994531f
+                                         : -__builtin_inff();
+  }
+  __syncthreads();
+  const int D4 = D / 4;
+  for (int e = tid; e < Hq * D4; e += blockDim.x) {
+    const int hh = e / D4, d4 = e % D4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < S1; ++s) {
+      const float wgt = sw[s * Hq + hh];
+      if (wgt != 0.f) {
+        const float4 o = *reinterpret_cast<const float4*>(
+            Opart + (s * plane + row0 + hh) * D + 4 * d4);
+        acc.x += wgt * o.x;
+        acc.y += wgt * o.y;
+        acc.z += wgt * o.z;
+        acc.w += wgt * o.w;
+      }
+    }
+    if constexpr (sizeof(OutT) == 2) {
+      uint2 pk = make_uint2((uint32_t)f32_to_bf16_bits(acc.x) |
+                                ((uint32_t)f32_to_bf16_bits(acc.y) << 16),
+                            (uint32_t)f32_to_bf16_bits(acc.z) |
+                                ((uint32_t)f32_to_bf16_bits(acc.w) << 16));
+      *reinterpret_cast<uint2*>(out + (row0 + hh) * D + 4 * d4) = pk;
+    } else {
+      *reinterpret_cast<float4*>(out + (row0 + hh) * D + 4 * d4) = acc;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -356,20 +478,21 @@ AttnPlan attention_plan(int batch, int N, int Hq, int Hkv, int D, int max_ctx, i
   const int G = Hq / Hkv;
   p.rows_per_kv = G * N;
   p.row_blocks = (p.rows_per_kv + 31) / 32;
-  p.mtiles = (p.row_blocks + kAttnMaxWaves - 1) / kAttnMaxWaves;
-  p.waves = (p.row_blocks + p.mtiles - 1) / p.mtiles;
-  const int tiles_ctx = std::max(1, (max_ctx + kTile - 1) / kTile);
+  p.waves = kAttnWaves;
+  p.mtiles = (p.row_blocks + kAttnWaves - 1) / kAttnWaves;
+  const int tiles_ctx = std::max(1, (max_ctx + kTileKeys - 1) / kTileKeys);
   int S = splits;
   if (S <= 0) {
-    // enough workgroups for ~2 per CU, at least 16 key tiles per split
+    // about four workgroups per CU (two resident), at least 8 key tiles
+    // (512 keys) per split so the partials stay well below the K/V bytes
     const int64_t wg_per_split = (int64_t)batch * Hkv * p.mtiles;
-    S = (int)std::max<int64_t>(1, (512 + wg_per_split - 1) / wg_per_split);
-    S = std::min(S, std::max(1, tiles_ctx / 16));
+    S = (int)std::max<int64_t>(1, (1024 + wg_per_split - 1) / wg_per_split);
+    S = std::min(S, std::max(1, tiles_ctx / 8));
   }
   S = std::max(1, std::min(S, tiles_ctx));
-  p.splits = S;
-  p.keys_per_split = ((tiles_ctx + S - 1) / S) * kTile;
-  const size_t rows = (size_t)(S + 1) * batch * N * Hq;
+  p.keys_per_split = ((tiles_ctx + S - 1) / S) * kTileKeys;
+  p.splits = (tiles_ctx * kTileKeys + p.keys_per_split - 1) / p.keys_per_split;
+  const size_t rows = (size_t)(p.splits + 1) * batch * N * Hq;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -385,8 +508,8 @@ AttnPlan attention_plan(int batch, int N, int Hq, int Hkv, int D, int max_ctx, i
 hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, const void* v,
                             bool bf16, const int* ctx_len, const uint64_t* anc,
                             const int* n_nodes, int batch, int N, int Hq, int Hkv, int D,
-                            int cap, int max_ctx, float scale, void* out, float* lse,
-                            void* ws, hipStream_t stream) {
+                            int cap, int max_ctx, float scale, void* out, bool out_f32,
+                            float* lse, void* ws, hipStream_t stream) {
   (void)max_ctx;
   const int64_t rows = (int64_t)batch * N * Hq;
   if (!bf16) {
@@ -402,22 +525,30 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, con
   float* Mpart = reinterpret_cast<float*>(w + p.off_ml);
   float* Lpart = Mpart + prow;
   const float scale_log2 = scale * 1.4426950408889634f;
-  dim3 grid(p.splits + 1, p.mtiles, batch * Hkv);
-  dim3 block(p.waves * WAVE);
+  const int items = batch * Hkv * p.mtiles * (p.splits + 1);
+  const int grid = 8 * ((items + 7) / 8);
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
   if (D == 128)
-    hipLaunchKernelGGL((k_attn_partial<128>), grid, block, 0, stream, q16, k16, v16, ctx_len,
-                       anc, n_nodes, N, Hq, Hkv, cap, p.splits, p.keys_per_split, scale_log2,
-                       Opart, Mpart, Lpart, batch);
+    hipLaunchKernelGGL((k_attn_partial<128>), dim3(grid), dim3(kAttnThreads), 0, stream, q16,
+                       k16, v16, ctx_len, anc, n_nodes, N, Hq, Hkv, cap, p.splits,
+                       p.keys_per_split, p.mtiles, items, scale_log2, Opart, Mpart, Lpart,
+                       batch);
   else
-    hipLaunchKernelGGL((k_attn_partial<64>), grid, block, 0, stream, q16, k16, v16, ctx_len,
-                       anc, n_nodes, N, Hq, Hkv, cap, p.splits, p.keys_per_split, scale_log2,
-                       Opart, Mpart, Lpart, batch);
-  hipLaunchKernelGGL((k_attn_combine<uint16_t>), dim3((unsigned)rows), dim3(128), 0, stream,
-                     Opart, Mpart, Lpart, n_nodes, batch, N, Hq, D, p.splits + 1,
-                     static_cast<uint16_t*>(out), lse);
+    hipLaunchKernelGGL((k_attn_partial<64>), dim3(grid), dim3(kAttnThreads), 0, stream, q16,
+                       k16, v16, ctx_len, anc, n_nodes, N, Hq, Hkv, cap, p.splits,
+                       p.keys_per_split, p.mtiles, items, scale_log2, Opart, Mpart, Lpart,
+                       batch);
+  const size_t lds = 3 * (size_t)(p.splits + 1) * Hq * sizeof(float);
+  if (out_f32)
+    hipLaunchKernelGGL((k_attn_combine<float>), dim3((unsigned)(batch * N)), dim3(256), lds,
+                       stream, Opart, Mpart, Lpart, n_nodes, batch, N, Hq, D, p.splits + 1,
+                       static_cast<float*>(out), lse);
+  else
+    hipLaunchKernelGGL((k_attn_combine<uint16_t>), dim3((unsigned)(batch * N)), dim3(256), lds,
+                       stream, Opart, Mpart, Lpart, n_nodes, batch, N, Hq, D, p.splits + 1,
+                       static_cast<uint16_t*>(out), lse);
   return hipGetLastError();
 }
 

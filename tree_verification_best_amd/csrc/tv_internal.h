@@ -51,8 +51,8 @@ AttnPlan attention_plan(int batch, int N, int Hq, int Hkv, int D, int max_ctx, i
 hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, const void* v,
                             bool bf16, const int* ctx_len, const uint64_t* anc,
                             const int* n_nodes, int batch, int N, int Hq, int Hkv, int D,
-                            int cap, int max_ctx, float scale, void* out, float* lse,
-                            void* ws, hipStream_t stream);
+                            int cap, int max_ctx, float scale, void* out, bool out_f32,
+                            float* lse, void* ws, hipStream_t stream);
 
 // ---- accept ----
 constexpr int kAcceptChunk = 4096;  // tokens per block in the logits passes
