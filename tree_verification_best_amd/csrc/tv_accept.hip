@@ -15,7 +15,7 @@
 //   k_walk    grid (batch)         the walk: children of the current node,
 //                                  acceptance draws, final draw by exact
 //                                  integer inverse CDF over the chunk sums
-// Rows past n_nodes are skipped; the walk only ever visits rows < n_nodes.
+// The passes read every row; the walk only ever visits rows < n_nodes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,40 +35,85 @@ __device__ __forceinline__ const T* row_ptr(const T* target, const T* draft, int
   return r < trows ? target + r * (int64_t)V : draft + (r - trows) * (int64_t)V;
 }
 
-__device__ __forceinline__ bool row_live(int64_t r, int64_t trows, int N,
-                                         const int* n_nodes) {
-  if (r >= trows) return true;
-  const int b = (int)(r / N), i = (int)(r % N);
-  return i < min(n_nodes[b], N);
-}
 
 // ---------------------------------------------------------------------------
+// Vector loads of a 4096-token chunk: thread t holds tokens
+// [base + t*16, base + t*16 + 16) (16 consecutive tokens, ids ascending).
+// fp32 rows load 4 x 16 bytes, bf16 rows 2 x 16 bytes, all issued before use.
+// Tokens past the end of the row are -inf.
+template <typename T>
+struct ChunkLoad;
+template <>
+struct ChunkLoad<float> {
+  static __device__ __forceinline__ void load(const float* p, int base, int V, float (&x)[16]) {
+    const int i0 = base + (int)threadIdx.x * 16;
+    if (i0 + 16 <= V && (V & 3) == 0) {
+      float4 a[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const float4*>(p + i0 + 4 * j);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[4 * j] = a[j].x;
+        x[4 * j + 1] = a[j].y;
+        x[4 * j + 2] = a[j].z;
+        x[4 * j + 3] = a[j].w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[j] = i0 + j < V ? p[i0 + j] : -__builtin_inff();
+    }
+  }
+};
+template <>
+struct ChunkLoad<uint16_t> {
+  static __device__ __forceinline__ void load(const uint16_t* p, int base, int V,
+                                              float (&x)[16]) {
+    const int i0 = base + (int)threadIdx.x * 16;
+    if (i0 + 16 <= V && (V & 7) == 0) {
+      uint4 a[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) a[j] = *reinterpret_cast<const uint4*>(p + i0 + 8 * j);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t w[4] = {a[j].x, a[j].y, a[j].z, a[j].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          x[8 * j + 2 * h] = __builtin_bit_cast(float, w[h] << 16);
+          x[8 * j + 2 * h + 1] = __builtin_bit_cast(float, w[h] & 0xFFFF0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        x[j] = i0 + j < V ? bf16_to_f32(p[i0 + j]) : -__builtin_inff();
+    }
+  }
+};
+
+// (max, argmax lowest id) of each 4096-token chunk of every row.  Rows past
+// n_nodes are read too (they are inside the array) and never used.
 template <typename T>
 __global__ __launch_bounds__(kAccNT) void k_rowmax(const T* __restrict__ target,
-                                                  const T* __restrict__ draft, int N, int V,
-                                                  int C, const int* __restrict__ n_nodes,
+                                                  const T* __restrict__ draft, int V, int C,
                                                   int64_t trows, float* __restrict__ cmax,
                                                   int* __restrict__ carg) {
   __shared__ float sv[kAccNT / WAVE];
   __shared__ int si[kAccNT / WAVE];
   const int c = blockIdx.x;
   const int64_t r = blockIdx.y;
-  if (!row_live(r, trows, N, n_nodes)) return;
   const T* p = row_ptr(target, draft, r, trows, V);
   const int base = c * kAcceptChunk;
-  float bv = -__builtin_inff();
-  int bi = 0x7fffffff;
+  float x[16];
+  ChunkLoad<T>::load(p, base, V, x);
+  float bv = x[0];
+  int bi = base + (int)threadIdx.x * 16;
 #pragma unroll
-  for (int e = 0; e < kAccE; ++e) {
-    const int idx = base + e * kAccNT + (int)threadIdx.x;
-    if (idx < V) {
-      const float x = Elem<T>::load(p, idx);
-      if (vi_better(x, idx, bv, bi)) {
-        bv = x;
-        bi = idx;
-      }
+  for (int j = 1; j < 16; ++j)
+    if (x[j] > bv) {  // strict: the lowest id among equal values stays
+      bv = x[j];
+      bi = base + (int)threadIdx.x * 16 + j;
     }
-  }
+  if (bi >= V) bi = 0x7fffffff;
   wave_argmax(bv, bi);
   if (lane_id() == 0) {
     sv[threadIdx.x / WAVE] = bv;
@@ -93,10 +138,12 @@ __device__ __forceinline__ float row_max_from_chunks(const float* cm, int C) {
   return wave_max_f(m);
 }
 
+// Fixed-point softmax mass of each chunk.  The chunk's logits are loaded
+// first; the row maximum (from the chunk maxima) arrives while they are in
+// flight.
 template <typename T>
 __global__ __launch_bounds__(kAccNT) void k_rowz(const T* __restrict__ target,
-                                                const T* __restrict__ draft, int N, int V,
-                                                int C, const int* __restrict__ n_nodes,
+                                                const T* __restrict__ draft, int V, int C,
                                                 int64_t trows, float inv_t,
                                                 const float* __restrict__ cmax,
                                                 uint64_t* __restrict__ cz) {
@@ -104,21 +151,19 @@ __global__ __launch_bounds__(kAccNT) void k_rowz(const T* __restrict__ target,
   __shared__ uint64_t wsum[kAccNT / WAVE];
   const int c = blockIdx.x;
   const int64_t r = blockIdx.y;
-  if (!row_live(r, trows, N, n_nodes)) return;
+  const T* p = row_ptr(target, draft, r, trows, V);
+  const int base = c * kAcceptChunk;
+  float x[16];
+  ChunkLoad<T>::load(p, base, V, x);
   if (threadIdx.x < WAVE) {
     const float m = row_max_from_chunks(cmax + r * C, C);
     if (threadIdx.x == 0) s_m = m;
   }
   __syncthreads();
   const float m = s_m;
-  const T* p = row_ptr(target, draft, r, trows, V);
-  const int base = c * kAcceptChunk;
   uint64_t acc = 0;
 #pragma unroll
-  for (int e = 0; e < kAccE; ++e) {
-    const int idx = base + e * kAccNT + (int)threadIdx.x;
-    if (idx < V) acc += weight(Elem<T>::load(p, idx), m, inv_t);
-  }
+  for (int j = 0; j < 16; ++j) acc += weight(x[j], m, inv_t);  // -inf padding weighs 0
   acc = wave_sum_u64(acc);
   if (lane_id() == 0) wsum[threadIdx.x / WAVE] = acc;
   __syncthreads();
@@ -533,11 +578,11 @@ static void launch_accept_t(const AcceptPlan& p, const T* target, const T* draft
   uint64_t* cz = sampled ? reinterpret_cast<uint64_t*>(w + p.off_cz) : nullptr;
   const int64_t trows = (int64_t)batch * N;
   dim3 g(p.C, (unsigned)p.rows);
-  hipLaunchKernelGGL((k_rowmax<T>), g, dim3(kAccNT), 0, stream, target, draft, N, V, p.C,
-                     n_nodes, trows, cmax, carg);
+  hipLaunchKernelGGL((k_rowmax<T>), g, dim3(kAccNT), 0, stream, target, draft, V, p.C, trows,
+                     cmax, carg);
   if (sampled)
-    hipLaunchKernelGGL((k_rowz<T>), g, dim3(kAccNT), 0, stream, target, draft, N, V, p.C,
-                       n_nodes, trows, inv_t, cmax, cz);
+    hipLaunchKernelGGL((k_rowz<T>), g, dim3(kAccNT), 0, stream, target, draft, V, p.C, trows,
+                       inv_t, cmax, cz);
   const int mode = !sampled ? kGreedy : (draft_proposal ? kDraft : kPointMass);
   hipLaunchKernelGGL((k_walk<T>), dim3(batch), dim3(kAccNT), 0, stream, target, draft, N, K,
                      V, p.C, parent, token, depth, n_nodes, mode, inv_t, seed, round,

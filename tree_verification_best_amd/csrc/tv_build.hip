@@ -49,18 +49,29 @@ __global__ __launch_bounds__(kBuildNT) void k_chunk_topk(const T* __restrict__ l
   const int64_t row = blockIdx.y;
   const T* p = logits + row * (int64_t)V;
   const int base = c * chunk;
+  // A full chunk: thread t holds the E consecutive tokens [base + t*E, ...)
+  // (16-byte loads).  The partial last chunk is spread across all threads
+  // (token base + e*NT + t), so that every lane holds real tokens when the
+  // chunk has at least NT of them.  Ids >= V are padding.
   float val[E];
   int id[E];
+  if (base + chunk <= V) {
+    const int i0 = base + (int)threadIdx.x * E;
+    load_run<E>(p, i0, V, val);
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    int idx = base + e * kBuildNT + (int)threadIdx.x;
-    bool ok = idx < V && (idx - base) < chunk;
-    val[e] = ok ? Elem<T>::load(p, idx) : -__builtin_inff();
-    id[e] = ok ? idx : V + idx;  // padding: distinct ids beyond the vocabulary
+    for (int e = 0; e < E; ++e) id[e] = i0 + e;
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int idx = base + e * kBuildNT + (int)threadIdx.x;
+      val[e] = idx < V ? Elem<T>::load(p, idx) : -__builtin_inff();
+      id[e] = idx;
+    }
   }
   float* ov = cval + (row * C + c) * (int64_t)k;
   int* oi = cid + (row * C + c) * (int64_t)k;
-  block_topk<kBuildNT, E>(val, id, k, sc, ov, oi);
+  // padding slots of a chunk with fewer than k tokens get ids unique per chunk
+  block_topk<kBuildNT, E>(val, id, k, sc, ov, oi, V, V + c * k);
 }
 
 // ---------------------------------------------------------------------------
@@ -73,6 +84,12 @@ __global__ __launch_bounds__(kBuildNT) void k_chunk_z(const T* __restrict__ logi
   __shared__ float s_m;
   const int c = blockIdx.x;
   const int64_t row = blockIdx.y;
+  // the chunk's logits first; the row maximum (over the chunk maxima, the
+  // first candidate of every chunk) arrives while they are in flight
+  const T* p = logits + row * (int64_t)V;
+  const int base = c * chunk;
+  float x[kBuildChunk / kBuildNT];
+  load_run<kBuildChunk / kBuildNT>(p, base + (int)threadIdx.x * (kBuildChunk / kBuildNT), V, x);
   if (threadIdx.x < WAVE) {
     float m = -__builtin_inff();
     for (int j = threadIdx.x; j < C; j += WAVE) m = fmaxf(m, cval[(row * C + j) * (int64_t)k]);
@@ -81,12 +98,9 @@ __global__ __launch_bounds__(kBuildNT) void k_chunk_z(const T* __restrict__ logi
   }
   __syncthreads();
   const float m = s_m;
-  const T* p = logits + row * (int64_t)V;
-  const int base = c * chunk;
-  const int end = min(V, base + chunk);
   uint64_t acc = 0;
-  for (int idx = base + (int)threadIdx.x; idx < end; idx += kBuildNT)
-    acc += weight(Elem<T>::load(p, idx), m, inv_t);
+#pragma unroll
+  for (int j = 0; j < kBuildChunk / kBuildNT; ++j) acc += weight(x[j], m, inv_t);
   acc = wave_sum_u64(acc);
   if (lane_id() == 0) wsum[threadIdx.x / WAVE] = acc;
   __syncthreads();
@@ -128,7 +142,7 @@ __global__ __launch_bounds__(kBuildNT) void k_finalize(int V, int C, int chunk, 
     z = wave_sum_u64(z);
     if (threadIdx.x == 0) s_z = z;
   }
-  block_topk<kBuildNT, E>(val, id, k, sc, tv, ti);  // ends with a barrier
+  block_topk<kBuildNT, E>(val, id, k, sc, tv, ti, V, V);  // ends with a barrier
   const float m = tv[0];                             // the row maximum
   const uint64_t Z = s_z;
   if ((int)threadIdx.x < k) {
@@ -150,6 +164,17 @@ __global__ __launch_bounds__(kBuildNT) void k_finalize(int V, int C, int chunk, 
 // ---------------------------------------------------------------------------
 // selection
 // ---------------------------------------------------------------------------
+// Workgroup-wide LDS hand-off.  A one-wave workgroup needs no s_barrier:
+// its LDS operations complete in issue order, so waiting for its own
+// outstanding ones is enough.
+template <int NT>
+__device__ __forceinline__ void block_sync() {
+  if constexpr (NT == WAVE)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  else
+    __syncthreads();
+}
+
 __device__ __forceinline__ bool sm_better(double as, uint64_t am, double bs, uint64_t bm) {
   return as > bs || (as == bs && am < bm);
 }
@@ -172,7 +197,7 @@ __device__ void bitonic_sort(double* s, KT* m, int n) {
           m[j] = mi;
         }
       }
-      __syncthreads();
+      block_sync<NT>();
     }
 }
 
@@ -192,7 +217,7 @@ __device__ void bitonic_merge(double* s, uint64_t* m, int n) {
         m[j] = mi;
       }
     }
-    __syncthreads();
+    block_sync<NT>();
   }
 }
 
@@ -201,7 +226,7 @@ __device__ int block_excl_scan(int v, int* wsum, int& total) {
   const int lane = lane_id(), wave = threadIdx.x / WAVE;
   int incl = wave_incl_scan_i(v);
   if (lane == WAVE - 1) wsum[wave] = incl;
-  __syncthreads();
+  block_sync<NT>();
   int woff = 0, tot = 0;
   for (int w = 0; w < NT / WAVE; ++w) {
     int x = wsum[w];
@@ -209,7 +234,7 @@ __device__ int block_excl_scan(int v, int* wsum, int& total) {
     tot += x;
   }
   total = tot;
-  __syncthreads();
+  block_sync<NT>();
   return woff + incl - v;
 }
 
@@ -284,7 +309,7 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
     ttab[i] = ftok[(int64_t)b * Kk + i];
   }
   if (threadIdx.x == 0) par_s[0] = 1.0;
-  __syncthreads();
+  block_sync<NT>();
 
   int g = 0, m_par = 1;
   bool have_kappa = false;
@@ -330,7 +355,7 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
       Cs[t] = -1.0;
       Ck[t] = 0xFFFFFFFFu;
     }
-    __syncthreads();
+    block_sync<NT>();
     bitonic_sort<NT, uint32_t>(Cs, Ck, Pn);
     const int l = min(total, B);
     const int Q = pow2ceil(max(g, l));
@@ -347,7 +372,7 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
         Mm[2 * Q - 1 - p] = ~0ull;
       }
     }
-    __syncthreads();
+    block_sync<NT>();
     bitonic_merge<NT>(Ms, Mm, 2 * Q);
     g = min(B, g + l);
     if (g == B) {
@@ -372,9 +397,9 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
   // ---- epilogue: rows in order, parents, ancestors ----
   const int n = g + 1;
   for (int d = threadIdx.x; d < K + 2; d += NT) dcnt[d] = 0;
-  __syncthreads();
+  block_sync<NT>();
   for (int p = threadIdx.x; p < g; p += NT) atomicAdd(&dcnt[meta_depth(Mm[p])], 1);
-  __syncthreads();
+  block_sync<NT>();
   if (threadIdx.x == 0) {
     int acc = 0;
     for (int d = 0; d < K + 2; ++d) {
@@ -383,12 +408,12 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
       acc += c;
     }
   }
-  __syncthreads();
+  block_sync<NT>();
   for (int p = threadIdx.x; p < g; p += NT) {
     const uint64_t mm = Mm[p];
     flat[dcnt[meta_depth(mm)] + meta_pos(mm)] = p + 1;
   }
-  __syncthreads();
+  block_sync<NT>();
   const int64_t rb = (int64_t)b * N;
   const int L = ctx_len[b];
   for (int j = threadIdx.x; j < N; j += NT) {
@@ -416,7 +441,7 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
     score[rb + j] = sc;
   }
   if (threadIdx.x == 0) n_nodes[b] = n;
-  __syncthreads();
+  block_sync<NT>();
   write_ancestors<NT>(rowpar, n, N, W, anc + rb * W);
 }
 
@@ -515,9 +540,15 @@ hipError_t launch_build(const BuildPlan& p, const void* draft, bool bf16, int ba
   }
   hipLaunchKernelGGL((k_finalize<kFinalizeE>), dim3((unsigned)p.rows), dim3(kBuildNT), 0,
                      stream, V, p.C, p.chunk, topk, inv_t, cval, cid, cz, ftok, fq);
-  hipLaunchKernelGGL((k_select<kBuildNT>), dim3(batch), dim3(kBuildNT), p.select_lds, stream,
-                     ftok, fq, K, topk, budget, p.P, p.Q2, root_token, ctx_len, parent, token,
-                     depth, pos, score, anc, n_nodes);
+  // small candidate sets: one wave, no workgroup barriers
+  if (p.P <= 512)
+    hipLaunchKernelGGL((k_select<WAVE>), dim3(batch), dim3(WAVE), p.select_lds, stream, ftok,
+                       fq, K, topk, budget, p.P, p.Q2, root_token, ctx_len, parent, token, depth,
+                       pos, score, anc, n_nodes);
+  else
+    hipLaunchKernelGGL((k_select<kBuildNT>), dim3(batch), dim3(kBuildNT), p.select_lds, stream,
+                       ftok, fq, K, topk, budget, p.P, p.Q2, root_token, ctx_len, parent, token,
+                       depth, pos, score, anc, n_nodes);
   return hipGetLastError();
 }
 

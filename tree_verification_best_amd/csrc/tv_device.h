@@ -113,6 +113,55 @@ struct Elem<uint16_t> {
   }
 };
 
+// E consecutive elements [i0, i0 + E) of a row as fp32, with 16-byte vector
+// loads when the run is inside the row and aligned; -inf past the end.
+template <typename T, int E>
+__device__ __forceinline__ void load_run(const T* p, int i0, int V, float (&x)[E]);
+
+template <int E>
+__device__ __forceinline__ void load_run(const float* p, int i0, int V, float (&x)[E]) {
+  static_assert(E % 4 == 0, "runs of whole float4s");
+  if (i0 + E <= V && ((i0 | V) & 3) == 0) {
+    float4 a[E / 4];
+#pragma unroll
+    for (int j = 0; j < E / 4; ++j) a[j] = *reinterpret_cast<const float4*>(p + i0 + 4 * j);
+#pragma unroll
+    for (int j = 0; j < E / 4; ++j) {
+      x[4 * j] = a[j].x;
+      x[4 * j + 1] = a[j].y;
+      x[4 * j + 2] = a[j].z;
+      x[4 * j + 3] = a[j].w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < E; ++j) x[j] = i0 + j < V ? p[i0 + j] : -__builtin_inff();
+  }
+}
+
+template <int E>
+__device__ __forceinline__ void load_run(const uint16_t* p, int i0, int V, float (&x)[E]) {
+  static_assert(E % 8 == 0, "runs of whole 16-byte vectors");
+  if (i0 + E <= V && ((i0 | V) & 7) == 0) {
+    uint4 a[E / 8];
+#pragma unroll
+    for (int j = 0; j < E / 8; ++j) a[j] = *reinterpret_cast<const uint4*>(p + i0 + 8 * j);
+#pragma unroll
+    for (int j = 0; j < E / 8; ++j) {
+      const uint32_t w[4] = {a[j].x, a[j].y, a[j].z, a[j].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        x[8 * j + 2 * h] = __builtin_bit_cast(float, w[h] << 16);
+        x[8 * j + 2 * h + 1] = __builtin_bit_cast(float, w[h] & 0xFFFF0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+      x[j] = i0 + j < V ? __builtin_bit_cast(float, (uint32_t)p[i0 + j] << 16)
+                        : -__builtin_inff();
+  }
+}
+
 // ---------------------------------------------------------------------------
 // wavefront helpers (wave64)
 // ---------------------------------------------------------------------------
@@ -198,6 +247,9 @@ __device__ __forceinline__ void wave_argmax(float& v, int& id) {
 // ---------------------------------------------------------------------------
 // Block-wide top-k (k <= 64) of E (value, id) items per thread, in the order
 // above.  Result: out_v / out_i [k] in LDS-or-global memory, best first.
+// Items with id >= first_pad are padding: they never enter the result; if
+// fewer than k real items exist, the remaining slots hold (-inf,
+// pad_base + slot).
 //
 // Each wave takes the k-th best of its 64 per-thread maxima as a threshold
 // (every item of the wave's top-k is at least as good, so the survivors
@@ -220,7 +272,8 @@ struct TopkScratch {
 
 template <int NT, int E>
 __device__ void block_topk(float (&val)[E], int (&id)[E], int k, TopkScratch<NT>& sc,
-                           float* out_v, int* out_i) {
+                           float* out_v, int* out_i, int first_pad = 0x7fffffff,
+                           int pad_base = 0x7fffffff) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
   constexpr int kCap = TopkScratch<NT>::kCap;
   if (tid == 0) sc.overflow = 0;
@@ -247,7 +300,7 @@ __device__ void block_topk(float (&val)[E], int (&id)[E], int k, TopkScratch<NT>
   // survivors: items at least as good as the threshold
   int cnt = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) cnt += vi_better(tv, ti, val[e], id[e]) ? 0 : 1;
+  for (int e = 0; e < E; ++e) cnt += (id[e] < first_pad && !vi_better(tv, ti, val[e], id[e])) ? 1 : 0;
   int incl = wave_incl_scan_i(cnt);
   int total = readlane_i(incl, WAVE - 1);
   __syncthreads();  // overflow flag initialised
@@ -257,7 +310,7 @@ __device__ void block_topk(float (&val)[E], int (&id)[E], int k, TopkScratch<NT>
     int off = incl - cnt;
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (!vi_better(tv, ti, val[e], id[e])) {
+      if (id[e] < first_pad && !vi_better(tv, ti, val[e], id[e])) {
         sc.sv[wave * kCap + off] = val[e];
         sc.si[wave * kCap + off] = id[e];
         ++off;
@@ -286,6 +339,10 @@ __device__ void block_topk(float (&val)[E], int (&id)[E], int k, TopkScratch<NT>
         out_i[r] = xi;
       }
     }
+    for (int r = nsurv + tid; r < k; r += NT) {
+      out_v[r] = -__builtin_inff();
+      out_i[r] = pad_base + r;
+    }
     __syncthreads();
     return;
   }
@@ -298,7 +355,7 @@ __device__ void block_topk(float (&val)[E], int (&id)[E], int k, TopkScratch<NT>
     int mi = 0x7fffffff;
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (!taken[e] && vi_better(val[e], id[e], mv, mi)) {
+      if (!taken[e] && id[e] < first_pad && vi_better(val[e], id[e], mv, mi)) {
         mv = val[e];
         mi = id[e];
       }
@@ -319,8 +376,9 @@ __device__ void block_topk(float (&val)[E], int (&id)[E], int k, TopkScratch<NT>
     for (int e = 0; e < E; ++e)
       if (id[e] == gi && val[e] == gv) taken[e] = true;
     if (tid == 0) {
-      out_v[r] = gv;
-      out_i[r] = gi;
+      const bool real = gi < first_pad;
+      out_v[r] = real ? gv : -__builtin_inff();
+      out_i[r] = real ? gi : pad_base + r;
     }
     __syncthreads();
   }
