@@ -317,9 +317,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
   }
 }
 
-// Merge the S + 1 partials of every query row of one (sequence, node):
-// weights 2^(m_s - M) / sum_s 2^(m_s - M) l_s, then a float4 sweep over
-// (head, d).
+// Merge the S + 1 partials of every query row: weights 2^(m_s - M) / L with
+// L = sum_s 2^(m_s - M) l_s.  One thread per (row, head, 4 output columns):
+// the D/4 threads of a row read the same (m_s, l_s) words, and every load of
+// a batch of splits is issued before the first is used.
 template <typename OutT>
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ Opart,
                                                      const float* __restrict__ Mpart,
@@ -328,74 +329,69 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
                                                      int N, int Hq, int D, int S1,
                                                      OutT* __restrict__ out,
                                                      float* __restrict__ lse) {
-  extern __shared__ float sw[];  // [S1][Hq] weights, then maxima and sums
-  const int bn = blockIdx.x;     // b * N + node
-  const int b = bn / N, node = bn % N;
-  const int64_t row0 = (int64_t)bn * Hq;
+  constexpr int kB = 8;  // splits per load batch
+  const int D4 = D / 4;
   const int64_t plane = (int64_t)batch * N * Hq;
-  const bool ok = node < min(n_nodes[b], N);
-  const int tid = threadIdx.x;
-  if (!ok) {
-    for (int e = tid; e < Hq * D; e += blockDim.x) {
-      if constexpr (sizeof(OutT) == 2)
-        out[row0 * D + e] = 0;
-      else
-        out[row0 * D + e] = 0.f;
-    }
-    if (lse)
-      for (int hh = tid; hh < Hq; hh += blockDim.x) lse[row0 + hh] = -__builtin_inff();
+  const int64_t r = (int64_t)blockIdx.x * (256 / D4) + threadIdx.x / D4;  // (b, node, head)
+  if (r >= plane) return;
+  const int d4 = threadIdx.x % D4;
+  const int64_t bn = r / Hq;
+  const int b = (int)(bn / N), node = (int)(bn % N);
+  OutT* dst = out + r * D + 4 * d4;
+  if (node >= min(n_nodes[b], N)) {
+    if constexpr (sizeof(OutT) == 2)
+      *reinterpret_cast<uint2*>(dst) = make_uint2(0u, 0u);
+    else
+      *reinterpret_cast<float4*>(dst) = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lse && d4 == 0) lse[r] = -__builtin_inff();
     return;
   }
-  // one round trip for every (split, head) pair of this node
-  float* sm = sw + S1 * Hq;
-  float* sl = sm + S1 * Hq;
-  for (int e = tid; e < S1 * Hq; e += blockDim.x) {
-    const int s = e / Hq, hh = e % Hq;
-    sm[e] = Mpart[s * plane + row0 + hh];
-    sl[e] = Lpart[s * plane + row0 + hh];
+  float M = -__builtin_inff();
+  for (int s0 = 0; s0 < S1; s0 += kB) {
+    float ms[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j)
+      ms[j] = s0 + j < S1 ? Mpart[(s0 + j) * plane + r] : -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < kB; ++j) M = fmaxf(M, ms[j]);
   }
-  __syncthreads();
-  for (int hh = tid; hh < Hq; hh += blockDim.x) {
-    float M = -__builtin_inff();
-    for (int s = 0; s < S1; ++s) M = fmaxf(M, sm[s * Hq + hh]);
-    float lsum = 0.f;
-    for (int s = 0; s < S1; ++s) {
-      const float ms = sm[s * Hq + hh];
-      const float wgt = ms == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-      sw[s * Hq + hh] = wgt;
-      lsum += wgt * sl[s * Hq + hh];
+  float lsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < S1; s0 += kB) {
+    float ms[kB], ls[kB];
+    float4 o[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const int s = min(s0 + j, S1 - 1);
+      ms[j] = Mpart[s * plane + r];
+      ls[j] = Lpart[s * plane + r];
+      o[j] = *reinterpret_cast<const float4*>(Opart + (s * plane + r) * D + 4 * d4);
     }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    for (int s = 0; s < S1; ++s) sw[s * Hq + hh] *= inv;
-    if (lse) lse[row0 + hh] = lsum > 0.f ? (M + log2f(lsum)) * 0.69314718055994531f
-                                         : -__builtin_inff();
-  }
-  __syncthreads();
-  const int D4 = D / 4;
-  for (int e = tid; e < Hq * D4; e += blockDim.x) {
-    const int hh = e / D4, d4 = e % D4;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < S1; ++s) {
-      const float wgt = sw[s * Hq + hh];
-      if (wgt != 0.f) {
-        const float4 o = *reinterpret_cast<const float4*>(
-            Opart + (s * plane + row0 + hh) * D + 4 * d4);
-        acc.x += wgt * o.x;
-        acc.y += wgt * o.y;
-        acc.z += wgt * o.z;
-        acc.w += wgt * o.w;
-      }
-    }
-    if constexpr (sizeof(OutT) == 2) {
-      uint2 pk = make_uint2((uint32_t)f32_to_bf16_bits(acc.x) |
-                                ((uint32_t)f32_to_bf16_bits(acc.y) << 16),
-                            (uint32_t)f32_to_bf16_bits(acc.z) |
-                                ((uint32_t)f32_to_bf16_bits(acc.w) << 16));
-      *reinterpret_cast<uint2*>(out + (row0 + hh) * D + 4 * d4) = pk;
-    } else {
-      *reinterpret_cast<float4*>(out + (row0 + hh) * D + 4 * d4) = acc;
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const bool live = s0 + j < S1 && ms[j] != -__builtin_inff();
+      const float wgt = live ? __builtin_amdgcn_exp2f(ms[j] - M) : 0.f;
+      lsum += wgt * ls[j];
+      acc.x += wgt * o[j].x;
+      acc.y += wgt * o[j].y;
+      acc.z += wgt * o[j].z;
+      acc.w += wgt * o[j].w;
     }
   }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  acc.x *= inv;
+  acc.y *= inv;
+  acc.z *= inv;
+  acc.w *= inv;
+  if constexpr (sizeof(OutT) == 2) {
+    *reinterpret_cast<uint2*>(dst) =
+        make_uint2((uint32_t)f32_to_bf16_bits(acc.x) | ((uint32_t)f32_to_bf16_bits(acc.y) << 16),
+                   (uint32_t)f32_to_bf16_bits(acc.z) | ((uint32_t)f32_to_bf16_bits(acc.w) << 16));
+  } else {
+    *reinterpret_cast<float4*>(dst) = acc;
+  }
+  if (lse && d4 == 0)
+    lse[r] = lsum > 0.f ? (M + log2f(lsum)) * 0.69314718055994531f : -__builtin_inff();
 }
 
 // ---------------------------------------------------------------------------
@@ -540,14 +536,14 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, con
                        k16, v16, ctx_len, anc, n_nodes, N, Hq, Hkv, cap, p.splits,
                        p.keys_per_split, p.mtiles, items, scale_log2, Opart, Mpart, Lpart,
                        batch);
-  const size_t lds = 3 * (size_t)(p.splits + 1) * Hq * sizeof(float);
+  const unsigned cgrid = (unsigned)((rows + (256 / (D / 4)) - 1) / (256 / (D / 4)));
   if (out_f32)
-    hipLaunchKernelGGL((k_attn_combine<float>), dim3((unsigned)(batch * N)), dim3(256), lds,
-                       stream, Opart, Mpart, Lpart, n_nodes, batch, N, Hq, D, p.splits + 1,
-                       static_cast<float*>(out), lse);
+    hipLaunchKernelGGL((k_attn_combine<float>), dim3(cgrid), dim3(256), 0, stream, Opart, Mpart,
+                       Lpart, n_nodes, batch, N, Hq, D, p.splits + 1, static_cast<float*>(out),
+                       lse);
   else
-    hipLaunchKernelGGL((k_attn_combine<uint16_t>), dim3((unsigned)(batch * N)), dim3(256), lds,
-                       stream, Opart, Mpart, Lpart, n_nodes, batch, N, Hq, D, p.splits + 1,
+    hipLaunchKernelGGL((k_attn_combine<uint16_t>), dim3(cgrid), dim3(256), 0, stream, Opart,
+                       Mpart, Lpart, n_nodes, batch, N, Hq, D, p.splits + 1,
                        static_cast<uint16_t*>(out), lse);
   return hipGetLastError();
 }
