@@ -36,6 +36,8 @@ CASES = [
     ("k64", 1, 3, 20000, 64, 200, 3.0, "f32"),
     ("deep", 1, 40, 700, 2, 300, 0.5, "f32"),
     ("peaked", 1, 12, 900, 3, 60, 12.0, "f32"),
+    ("budget-512", 1, 30, 500, 2, 512, 0.7, "f32"),
+    ("mid-bf16", 2, 8, 4000, 16, 256, 3.0, "bf16"),
 ]
 
 

@@ -24,8 +24,14 @@
 //     among the B best if (i+1)(r+1) <= B.  Once B nodes are known, a
 //     candidate also needs a score above the B-th best (it is deeper than
 //     everything chosen so far, so a tie loses);
-//   * candidates are bitonic-sorted in LDS into level order, and merged with
-//     the running best-B list (bitonic merge); the first B are kept.
+//   * candidates are put in level order by rank: the rank of a candidate is
+//     the number of candidates ahead of it, counted by all workgroup lanes
+//     over slices of the list (a depth with more than kRankMax candidates is
+//     bitonic-sorted in LDS instead);
+//   * the running best-B list and the depth's list are merged by rank too:
+//     an item's new place is its place in its own list plus the number of
+//     items of the other list ahead of it (a binary search; a best-list item
+//     goes first on equal scores, as it is shallower); the first B are kept.
 // When a depth adds nothing, no deeper node can enter.  The result is the
 // exact B-best set in order.
 #include <hip/hip_runtime.h>
@@ -201,26 +207,6 @@ __device__ void bitonic_sort(double* s, KT* m, int n) {
     }
 }
 
-// n elements holding a best-first half followed by a worst-first half
-template <int NT>
-__device__ void bitonic_merge(double* s, uint64_t* m, int n) {
-  for (int stride = n >> 1; stride > 0; stride >>= 1) {
-    for (int t = threadIdx.x; t < (n >> 1); t += NT) {
-      int i = 2 * t - (t & (stride - 1));
-      int j = i + stride;
-      double si = s[i], sj = s[j];
-      uint64_t mi = m[i], mj = m[j];
-      if (sm_better(sj, mj, si, mi)) {
-        s[i] = sj;
-        s[j] = si;
-        m[i] = mj;
-        m[j] = mi;
-      }
-    }
-    block_sync<NT>();
-  }
-}
-
 template <int NT>
 __device__ int block_excl_scan(int v, int* wsum, int& total) {
   const int lane = lane_id(), wave = threadIdx.x / WAVE;
@@ -276,11 +262,30 @@ __device__ void write_ancestors(const int* par, int n, int N, int W, uint64_t* a
   }
 }
 
+__device__ __forceinline__ int pow2floor(int x) {
+  int p = 1;
+  while (2 * p <= x) p <<= 1;
+  return x > 0 ? p : 0;
+}
+
+// number of the first n items of a best-first list (s) with s > x, or
+// s >= x when or_equal: a binary search of fixed length
+__device__ __forceinline__ int count_ahead(const double* s, int n, double x, bool or_equal) {
+  int at = 0;
+  for (int step = pow2floor(n); step > 0; step >>= 1) {
+    const int t = at + step;
+    if (t <= n) {
+      const double y = s[t - 1];
+      if (y > x || (or_equal && y == x)) at = t;
+    }
+  }
+  return at;
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
                                               const double* __restrict__ fq, int K, int k,
-                                              int B, int P, int Q2,
-                                              const int* __restrict__ root_token,
+                                              int B, int P, const int* __restrict__ root_token,
                                               const int* __restrict__ ctx_len,
                                               int* __restrict__ parent, int* __restrict__ token,
                                               int* __restrict__ depth, int* __restrict__ pos,
@@ -288,135 +293,173 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
                                               uint64_t* __restrict__ anc,
                                               int* __restrict__ n_nodes) {
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int wsum[NT / WAVE];
+  __shared__ int s_kept[2];
+  constexpr int NW = NT / WAVE;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
   const int b = blockIdx.x;
   const int N = B + 1;
   const int W = (N + 63) / 64;
   const int Kk = K * k;
-  double* qtab = reinterpret_cast<double*>(smem);
-  double* Ms = qtab + Kk;
-  double* Cs = Ms + Q2;
-  double* par_s = Cs + P;
-  uint64_t* Mm = reinterpret_cast<uint64_t*>(par_s + N);
-  uint32_t* Ck = reinterpret_cast<uint32_t*>(Mm + Q2);
-  int* ttab = reinterpret_cast<int*>(Ck + P);
-  int* rowpar = ttab + Kk;            // [N] parent rows (epilogue)
-  int* flat = rowpar + N;             // [N] row of (depth, position)
-  int* dcnt = flat + N;               // [K + 2] per-depth counts / offsets
-  __shared__ int wsum[NT / WAVE];
+  const int R = min(P, kRankMax);
+  double* qtab = reinterpret_cast<double*>(smem);  // [Kk] candidate probabilities
+  double* gs_a = qtab + Kk;                        // [B] best list, two buffers
+  double* gs_b = gs_a + B;
+  double* Cs = gs_b + B;                           // [P] candidates of one depth
+  double* Ls = Cs + P;                             // [B] the depth's level order; next parents
+  uint64_t* gm_a = reinterpret_cast<uint64_t*>(Ls + B);
+  uint64_t* gm_b = gm_a + B;
+  uint32_t* Ck = reinterpret_cast<uint32_t*>(gm_b + B);  // [P] parent << 16 | rank
+  uint32_t* Lk = Ck + P;                                 // [B]
+  int* rk = reinterpret_cast<int*>(Lk + B);              // [R] ranks
+  int* ttab = rk + R;                                    // [Kk]
+  int* rowpar = ttab + Kk;                               // [N]
+  int* flat = rowpar + N;                                // [N]
+  int* dcnt = flat + N;                                  // [K + 2]
 
-  for (int i = threadIdx.x; i < Kk; i += NT) {
+  for (int i = tid; i < Kk; i += NT) {
     qtab[i] = fq[(int64_t)b * Kk + i];
     ttab[i] = ftok[(int64_t)b * Kk + i];
   }
-  if (threadIdx.x == 0) par_s[0] = 1.0;
-  block_sync<NT>();
+  for (int i = tid; i < R; i += NT) rk[i] = 0;
+  if (tid == 0) {
+    Ls[0] = 1.0;  // the root, sole parent of depth 1
+    s_kept[0] = s_kept[1] = 0;
+  }
+  __syncthreads();
 
+  double* Gs = gs_a;
+  double* Gs_n = gs_b;
+  uint64_t* Gm = gm_a;
+  uint64_t* Gm_n = gm_b;
   int g = 0, m_par = 1;
   bool have_kappa = false;
   double kappa = 0.0;
   for (int d = 1; d <= K && B > 0; ++d) {
     const double* qd = qtab + (d - 1) * k;
-    const int ppt = (m_par + NT - 1) / NT;
-    // children of each parent that can still be among the B best
-    int my = 0;
-    for (int j = 0; j < ppt; ++j) {
-      const int i = threadIdx.x * ppt + j;
-      if (i < m_par) {
-        const int lim = min(k, B / (i + 1));
-        const double si = par_s[i];
-        int c = 0;
-        while (c < lim) {
-          const double s = si * qd[c];
-          if (have_kappa && !(s > kappa)) break;
-          ++c;
-        }
-        my += c;
+    // ---- candidates: a prefix of every parent's children
+    int total = 0;
+    for (int i0 = 0; i0 < m_par; i0 += NT) {
+      const int i = i0 + tid;
+      const double si = i < m_par ? Ls[i] : 0.0;
+      const int lim = i < m_par ? min(k, B / (i + 1)) : 0;
+      int cnt = 0;
+      while (cnt < lim) {
+        const double sc = si * qd[cnt];
+        if (have_kappa && !(sc > kappa)) break;
+        ++cnt;
       }
+      int tot;
+      const int off = total + block_excl_scan<NT>(cnt, wsum, tot);
+      for (int c = 0; c < cnt; ++c) {
+        Cs[off + c] = si * qd[c];
+        Ck[off + c] = ((uint32_t)i << 16) | (uint32_t)c;
+      }
+      total += tot;
     }
-    int total;
-    int off = block_excl_scan<NT>(my, wsum, total);
     if (total == 0) break;
-    for (int j = 0; j < ppt; ++j) {
-      const int i = threadIdx.x * ppt + j;
-      if (i < m_par) {
-        const int lim = min(k, B / (i + 1));
-        const double si = par_s[i];
-        for (int c = 0; c < lim; ++c) {
-          const double s = si * qd[c];
-          if (have_kappa && !(s > kappa)) break;
-          Cs[off] = s;
-          Ck[off] = ((uint32_t)i << 16) | (uint32_t)c;
-          ++off;
+    if (tid == 0) s_kept[(d + 1) & 1] = 0;
+    __syncthreads();
+    const int l = min(total, B);
+    if (total <= kRankMax) {
+      // ---- level order by rank: wave w counts over its slice of the list
+      const int slice = (total + NW - 1) / NW;
+      const int i_lo = wave * slice, i_hi = min(total, i_lo + slice);
+      for (int j0 = 0; j0 < total; j0 += WAVE) {
+        const int j = min(j0 + lane, total - 1);
+        const double xs = Cs[j];
+        const uint32_t xk = Ck[j];
+        int ahead = 0;
+        for (int i = i_lo; i < i_hi; ++i) {
+          const double ys = Cs[i];
+          const uint32_t yk = Ck[i];
+          ahead += (int)(ys > xs) | ((int)(ys == xs) & (int)(yk < xk));
+        }
+        if (j0 + lane < total && ahead > 0) atomicAdd(&rk[j], ahead);
+      }
+      __syncthreads();
+      for (int j = tid; j < total; j += NT) {
+        const int r = rk[j];
+        rk[j] = 0;
+        if (r < l) {
+          Ls[r] = Cs[j];
+          Lk[r] = Ck[j];
         }
       }
-    }
-    const int Pn = pow2ceil(total);
-    for (int t = total + threadIdx.x; t < Pn; t += NT) {
-      Cs[t] = -1.0;
-      Ck[t] = 0xFFFFFFFFu;
-    }
-    block_sync<NT>();
-    bitonic_sort<NT, uint32_t>(Cs, Ck, Pn);
-    const int l = min(total, B);
-    const int Q = pow2ceil(max(g, l));
-    for (int p = threadIdx.x; p < Q; p += NT) {
-      if (p >= g) {
-        Ms[p] = -1.0;
-        Mm[p] = ~0ull;
+    } else {
+      const int Pn = pow2ceil(total);
+      for (int t = total + tid; t < Pn; t += NT) {
+        Cs[t] = -1.0;
+        Ck[t] = 0xFFFFFFFFu;
       }
-      if (p < l) {
-        Ms[2 * Q - 1 - p] = Cs[p];
-        Mm[2 * Q - 1 - p] = ((uint64_t)d << 48) | ((uint64_t)p << 32) | (uint64_t)Ck[p];
-      } else {
-        Ms[2 * Q - 1 - p] = -1.0;
-        Mm[2 * Q - 1 - p] = ~0ull;
+      __syncthreads();
+      bitonic_sort<NT, uint32_t>(Cs, Ck, Pn);
+      for (int j = tid; j < l; j += NT) {
+        Ls[j] = Cs[j];
+        Lk[j] = Ck[j];
       }
     }
-    block_sync<NT>();
-    bitonic_merge<NT>(Ms, Mm, 2 * Q);
+    __syncthreads();
+
+    // ---- merge into the best list
+    for (int a = tid; a < g; a += NT) {
+      const double x = Gs[a];
+      const int np = a + count_ahead(Ls, l, x, false);
+      if (np < B) {
+        Gs_n[np] = x;
+        Gm_n[np] = Gm[a];
+      }
+    }
+    int last_kept = 0;
+    for (int c = tid; c < l; c += NT) {
+      const double x = Ls[c];
+      const int np = c + count_ahead(Gs, g, x, true);
+      if (np < B) {
+        Gs_n[np] = x;
+        Gm_n[np] = ((uint64_t)d << 48) | ((uint64_t)c << 32) | (uint64_t)Lk[c];
+        last_kept = c + 1;  // kept candidates are a prefix of the level order
+      }
+    }
+    if (last_kept > 0) atomicMax(&s_kept[d & 1], last_kept);
+    __syncthreads();
     g = min(B, g + l);
     if (g == B) {
       have_kappa = true;
-      kappa = Ms[B - 1];
+      kappa = Gs_n[B - 1];
     }
-    // next parents: the depth-d nodes kept, at their level positions
-    int cnt = 0;
-    for (int p = threadIdx.x; p < g; p += NT) {
-      const uint64_t mm = Mm[p];
-      if (meta_depth(mm) == d) {
-        par_s[meta_pos(mm)] = Ms[p];
-        ++cnt;
-      }
-    }
-    int tot2;
-    (void)block_excl_scan<NT>(cnt, wsum, tot2);
-    m_par = tot2;
+    double* ts = Gs;
+    Gs = Gs_n;
+    Gs_n = ts;
+    uint64_t* tm = Gm;
+    Gm = Gm_n;
+    Gm_n = tm;
+    m_par = s_kept[d & 1];  // the kept depth-d nodes, Ls[0..m_par), parent the next depth
     if (m_par == 0) break;
   }
 
-  // ---- epilogue: rows in order, parents, ancestors ----
+  // ---- epilogue: rows in best-first order, parents, ancestors ----
   const int n = g + 1;
-  for (int d = threadIdx.x; d < K + 2; d += NT) dcnt[d] = 0;
-  block_sync<NT>();
-  for (int p = threadIdx.x; p < g; p += NT) atomicAdd(&dcnt[meta_depth(Mm[p])], 1);
-  block_sync<NT>();
-  if (threadIdx.x == 0) {
+  for (int dd = tid; dd < K + 2; dd += NT) dcnt[dd] = 0;
+  __syncthreads();
+  for (int p = tid; p < g; p += NT) atomicAdd(&dcnt[meta_depth(Gm[p])], 1);
+  __syncthreads();
+  if (tid == 0) {
     int acc = 0;
-    for (int d = 0; d < K + 2; ++d) {
-      int c = dcnt[d];
-      dcnt[d] = acc;  // offset of depth d in `flat`
+    for (int dd = 0; dd < K + 2; ++dd) {
+      const int c = dcnt[dd];
+      dcnt[dd] = acc;  // offset of depth dd in `flat`
       acc += c;
     }
   }
-  block_sync<NT>();
-  for (int p = threadIdx.x; p < g; p += NT) {
-    const uint64_t mm = Mm[p];
+  __syncthreads();
+  for (int p = tid; p < g; p += NT) {
+    const uint64_t mm = Gm[p];
     flat[dcnt[meta_depth(mm)] + meta_pos(mm)] = p + 1;
   }
-  block_sync<NT>();
+  __syncthreads();
   const int64_t rb = (int64_t)b * N;
   const int L = ctx_len[b];
-  for (int j = threadIdx.x; j < N; j += NT) {
+  for (int j = tid; j < N; j += NT) {
     int pa = -1, to = -1, de = -1, po = -1;
     double sc = 0.0;
     if (j == 0) {
@@ -425,13 +468,13 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
       po = L;
       sc = 1.0;
     } else if (j < n) {
-      const uint64_t mm = Mm[j - 1];
-      const int d = meta_depth(mm);
-      pa = d == 1 ? 0 : flat[min(dcnt[d - 1] + meta_parent(mm), N - 1)];
-      to = ttab[(d - 1) * k + meta_rank(mm)];
-      de = d;
-      po = L + d;
-      sc = Ms[j - 1];
+      const uint64_t mm = Gm[j - 1];
+      const int dd = meta_depth(mm);
+      pa = dd == 1 ? 0 : flat[min(dcnt[dd - 1] + meta_parent(mm), N - 1)];
+      to = ttab[(dd - 1) * k + meta_rank(mm)];
+      de = dd;
+      po = L + dd;
+      sc = Gs[j - 1];
     }
     rowpar[j] = pa;
     parent[rb + j] = pa;
@@ -440,8 +483,8 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
     pos[rb + j] = po;
     score[rb + j] = sc;
   }
-  if (threadIdx.x == 0) n_nodes[b] = n;
-  block_sync<NT>();
+  if (tid == 0) n_nodes[b] = n;
+  __syncthreads();
   write_ancestors<NT>(rowpar, n, N, W, anc + rb * W);
 }
 
@@ -492,12 +535,11 @@ BuildPlan build_plan(int batch, int K, int V, int topk, int budget) {
   int64_t cmax = 0;
   for (int i = 0; i < budget; ++i) cmax += std::min(topk, budget / (i + 1));
   p.P = pow2ceil((int)std::max<int64_t>(cmax, 1));
-  p.Q2 = 2 * pow2ceil(std::max(budget, 1));
   const int N = budget + 1;
   const int Kk = K * topk;
-  p.select_lds = (size_t)Kk * 8 + (size_t)p.Q2 * 8 + (size_t)p.P * 8 + (size_t)N * 8 +
-                 (size_t)p.Q2 * 8 + (size_t)p.P * 4 + (size_t)Kk * 4 + (size_t)N * 4 * 2 +
-                 (size_t)(K + 2) * 4 + 64;
+  const int R = std::min(p.P, kRankMax);
+  p.select_lds = (size_t)8 * (Kk + 3 * (size_t)budget + p.P) + (size_t)16 * budget +
+                 (size_t)4 * (p.P + budget + R + Kk + 2 * (size_t)N + K + 2);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -540,15 +582,9 @@ hipError_t launch_build(const BuildPlan& p, const void* draft, bool bf16, int ba
   }
   hipLaunchKernelGGL((k_finalize<kFinalizeE>), dim3((unsigned)p.rows), dim3(kBuildNT), 0,
                      stream, V, p.C, p.chunk, topk, inv_t, cval, cid, cz, ftok, fq);
-  // small candidate sets: one wave, no workgroup barriers
-  if (p.P <= 512)
-    hipLaunchKernelGGL((k_select<WAVE>), dim3(batch), dim3(WAVE), p.select_lds, stream, ftok,
-                       fq, K, topk, budget, p.P, p.Q2, root_token, ctx_len, parent, token, depth,
-                       pos, score, anc, n_nodes);
-  else
-    hipLaunchKernelGGL((k_select<kBuildNT>), dim3(batch), dim3(kBuildNT), p.select_lds, stream,
-                       ftok, fq, K, topk, budget, p.P, p.Q2, root_token, ctx_len, parent, token,
-                       depth, pos, score, anc, n_nodes);
+  hipLaunchKernelGGL((k_select<kBuildNT>), dim3(batch), dim3(kBuildNT), p.select_lds, stream,
+                     ftok, fq, K, topk, budget, p.P, root_token, ctx_len, parent, token, depth,
+                     pos, score, anc, n_nodes);
   return hipGetLastError();
 }
 

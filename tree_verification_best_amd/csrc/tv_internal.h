@@ -14,12 +14,13 @@ namespace tvk {
 
 // ---- build ----
 constexpr int kBuildChunk = 8192;  // tokens per block in the draft-row passes
+constexpr int kRankMax = 512;  // depth lists up to this size are ordered by rank counting
 constexpr int kFinalizeE = 8;      // per-thread items when merging chunk candidates
 
 struct BuildPlan {
   int chunk, C;
   int64_t rows;
-  int P, Q2;  // LDS sort buffer (candidates of one depth) and merge buffer sizes
+  int P;  // LDS room for the candidates of one depth (a power of two)
   size_t select_lds;
   size_t off_cval, off_cid, off_cz, off_ftok, off_fq;
   size_t workspace;
