@@ -210,7 +210,7 @@ __device__ void bitonic_sort(double* s, KT* m, int n) {
 template <int NT>
 __device__ int block_excl_scan(int v, int* wsum, int& total) {
   const int lane = lane_id(), wave = threadIdx.x / WAVE;
-  int incl = wave_incl_scan_i(v);
+  int incl = wave_scan_add_dpp(v);
   if (lane == WAVE - 1) wsum[wave] = incl;
   block_sync<NT>();
   int woff = 0, tot = 0;
@@ -268,16 +268,23 @@ __device__ __forceinline__ int pow2floor(int x) {
   return x > 0 ? p : 0;
 }
 
-// number of the first n items of a best-first list (s) with s > x, or
-// s >= x when or_equal: a binary search of fixed length
+// Number of the first n items of a best-first list (s) with s > x, or
+// s >= x when or_equal.  The predicate holds on a prefix, so an 8-way search
+// finds it: each round reads 8 probes, stride apart, all issued together.
 __device__ __forceinline__ int count_ahead(const double* s, int n, double x, bool or_equal) {
+  if (n <= 0) return 0;
+  int stride = 1;
+  while (stride * 8 < n) stride *= 8;
   int at = 0;
-  for (int step = pow2floor(n); step > 0; step >>= 1) {
-    const int t = at + step;
-    if (t <= n) {
-      const double y = s[t - 1];
-      if (y > x || (or_equal && y == x)) at = t;
-    }
+  for (; stride > 0; stride >>= 3) {
+    double y[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) y[u] = s[min(at + stride * (u + 1), n) - 1];
+    int adv = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      adv += (at + stride * (u + 1) <= n && (y[u] > x || (or_equal && y[u] == x))) ? 1 : 0;
+    at += adv * stride;
   }
   return at;
 }
@@ -343,17 +350,30 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
       const int i = i0 + tid;
       const double si = i < m_par ? Ls[i] : 0.0;
       const int lim = i < m_par ? min(k, B / (i + 1)) : 0;
+      // children that pass form a prefix (scores fall with the rank); the
+      // q values are read eight at a time
       int cnt = 0;
-      while (cnt < lim) {
-        const double sc = si * qd[cnt];
-        if (have_kappa && !(sc > kappa)) break;
-        ++cnt;
+      for (int c0 = 0; c0 < k; c0 += 8) {
+        double qq[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) qq[u] = qd[min(c0 + u, k - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          cnt += (c0 + u < lim && (!have_kappa || si * qq[u] > kappa)) ? 1 : 0;
+        if (!__any(cnt == c0 + 8 && c0 + 8 < lim)) break;
       }
       int tot;
       const int off = total + block_excl_scan<NT>(cnt, wsum, tot);
-      for (int c = 0; c < cnt; ++c) {
-        Cs[off + c] = si * qd[c];
-        Ck[off + c] = ((uint32_t)i << 16) | (uint32_t)c;
+      for (int c0 = 0; c0 < cnt; c0 += 8) {
+        double qq[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) qq[u] = qd[min(c0 + u, k - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (c0 + u < cnt) {
+            Cs[off + c0 + u] = si * qq[u];
+            Ck[off + c0 + u] = ((uint32_t)i << 16) | (uint32_t)(c0 + u);
+          }
       }
       total += tot;
     }
@@ -370,10 +390,19 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
         const double xs = Cs[j];
         const uint32_t xk = Ck[j];
         int ahead = 0;
-        for (int i = i_lo; i < i_hi; ++i) {
-          const double ys = Cs[i];
-          const uint32_t yk = Ck[i];
-          ahead += (int)(ys > xs) | ((int)(ys == xs) & (int)(yk < xk));
+        for (int i0 = i_lo; i0 < i_hi; i0 += 8) {
+          double ys[8];
+          uint32_t yk[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = min(i0 + u, i_hi - 1);
+            ys[u] = Cs[i];
+            yk[u] = Ck[i];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            ahead += (i0 + u < i_hi) &
+                     ((int)(ys[u] > xs) | ((int)(ys[u] == xs) & (int)(yk[u] < xk)));
         }
         if (j0 + lane < total && ahead > 0) atomicAdd(&rk[j], ahead);
       }
@@ -401,26 +430,30 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
     }
     __syncthreads();
 
-    // ---- merge into the best list
-    for (int a = tid; a < g; a += NT) {
-      const double x = Gs[a];
-      const int np = a + count_ahead(Ls, l, x, false);
-      if (np < B) {
-        Gs_n[np] = x;
-        Gm_n[np] = Gm[a];
-      }
-    }
+    // ---- merge into the best list: items 0..g-1 are the best list, g..g+l-1
+    // the depth's list
     int last_kept = 0;
-    for (int c = tid; c < l; c += NT) {
-      const double x = Ls[c];
-      const int np = c + count_ahead(Gs, g, x, true);
-      if (np < B) {
-        Gs_n[np] = x;
-        Gm_n[np] = ((uint64_t)d << 48) | ((uint64_t)c << 32) | (uint64_t)Lk[c];
-        last_kept = c + 1;  // kept candidates are a prefix of the level order
+    for (int t = tid; t < g + l; t += NT) {
+      if (t < g) {
+        const double x = Gs[t];
+        const int np = t + count_ahead(Ls, l, x, false);
+        if (np < B) {
+          Gs_n[np] = x;
+          Gm_n[np] = Gm[t];
+        }
+      } else {
+        const int c = t - g;
+        const double x = Ls[c];
+        const int np = c + count_ahead(Gs, g, x, true);
+        if (np < B) {
+          Gs_n[np] = x;
+          Gm_n[np] = ((uint64_t)d << 48) | ((uint64_t)c << 32) | (uint64_t)Lk[c];
+          last_kept = c + 1;  // kept candidates are a prefix of the level order
+        }
       }
     }
-    if (last_kept > 0) atomicMax(&s_kept[d & 1], last_kept);
+    last_kept = __builtin_amdgcn_readlane(wave_scan_max_dpp(last_kept), WAVE - 1);
+    if (lane == 0 && last_kept > 0) atomicMax(&s_kept[d & 1], last_kept);
     __syncthreads();
     g = min(B, g + l);
     if (g == B) {

@@ -217,6 +217,31 @@ __device__ __forceinline__ int wave_incl_scan_i(int v) {
   }
   return v;
 }
+// Inclusive scans over the wave by DPP row shifts (within rows of 16 lanes)
+// and row broadcasts (lane 15 into the next row, lane 31 into rows 2 and 3);
+// lanes with no source read 0.  For non-negative ints (sum and max).
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, true);
+}
+__device__ __forceinline__ int wave_scan_add_dpp(int v) {
+  v += dpp_i<0x111>(v);       // row_shr:1
+  v += dpp_i<0x112>(v);       // row_shr:2
+  v += dpp_i<0x114>(v);       // row_shr:4
+  v += dpp_i<0x118>(v);       // row_shr:8
+  v += dpp_i<0x142, 0xA>(v);  // row_bcast:15
+  v += dpp_i<0x143, 0xC>(v);  // row_bcast:31
+  return v;
+}
+__device__ __forceinline__ int wave_scan_max_dpp(int v) {
+  v = max(v, dpp_i<0x111>(v));
+  v = max(v, dpp_i<0x112>(v));
+  v = max(v, dpp_i<0x114>(v));
+  v = max(v, dpp_i<0x118>(v));
+  v = max(v, dpp_i<0x142, 0xA>(v));
+  v = max(v, dpp_i<0x143, 0xC>(v));
+  return v;
+}
 __device__ __forceinline__ float wave_max_f(float v) {
 #pragma unroll
   for (int m = 1; m < WAVE; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
