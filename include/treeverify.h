@@ -162,7 +162,8 @@ tv_status tv_tree_ancestors(const int32_t *parent, const int32_t *n_nodes,
  *   splits   number of context splits (0 = automatic); partial results are
  *            merged with their log-sum-exp weights.
  *   Rows past n_nodes: out 0, lse -inf.
- * Limits: D in {64, 128}; Hq % Hkv == 0; N <= 1024; max_ctx + N <= cap.
+ * Limits: D in {64, 128}; Hq % Hkv == 0; N <= 1024; max_ctx + N <= cap;
+ *         one head's cache rows (cap * D * 2 bytes) below 2 GiB (TV_ERR_UNSUPPORTED).
  * bf16: bf16 products on the matrix cores with fp32 accumulation and an
  * fp32 online softmax; the softmax weights enter the second product
  * rounded to bf16 while the normaliser sums them in fp32.  f32: fp32

@@ -117,6 +117,7 @@ tv_status tv_tree_attention_verify(const void* q, const void* k_cache, const voi
   if ((int64_t)max_ctx + N > (int64_t)cap) return TV_ERR_INVALID;
   if (!attn_args_ok(batch, N, Hq, Hkv, D, max_ctx, splits)) return TV_ERR_UNSUPPORTED;
   if ((int64_t)batch * Hkv > kMaxGridY) return TV_ERR_UNSUPPORTED;
+  if ((int64_t)cap * D * 2 > 0x7FFFFFFF) return TV_ERR_UNSUPPORTED;  // one head's rows: 32-bit offsets
   const tvk::AttnPlan p = tvk::attention_plan(batch, N, Hq, Hkv, D, max_ctx, splits);
   if (dt == TV_BF16 && (!workspace || workspace_bytes < p.workspace)) return TV_ERR_WORKSPACE;
   return device_status(tvk::launch_attention(p, q, k_cache, v_cache, dt == TV_BF16, ctx_len,

@@ -16,7 +16,10 @@
 //     lane l ^ 32;
 //   * O^T += V^T P^T with the same instruction: P^T leaves the registers of
 //     the S^T accumulator as the B operand directly (same lane = same row);
-//     V is stored transposed in LDS so the A operand is two 8-byte reads;
+//     V is staged row-major, as it sits in the cache, and the A operand
+//     (8 keys of one d per lane) comes from two transposing LDS reads
+//     (ds_read_b64_tr_b16: within each 16-lane group, lane 4p + q receives
+//     element q of the 8-byte rows addressed by lanes p, p + 4, p + 8, p + 12);
 //   * split-K over the context: split s < S covers keys [s*KS, (s+1)*KS), the
 //     extra split S covers the tree keys with the ancestor mask (the only
 //     masked tile); partials (m, l, O) go to the workspace and k_combine
@@ -37,6 +40,16 @@ constexpr int kTileKeys = 64;  // keys staged per iteration (two 32-key MFMA sub
 constexpr int kAttnWaves = 4;  // waves per workgroup, 32 query rows each
 constexpr int kAttnThreads = kAttnWaves * WAVE;
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// transposing 8-byte LDS read (see the layout note above)
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<lds_s16x4*>(reinterpret_cast<uintptr_t>(p) & 0xFFFFFFFFu));
+}
+
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   __bf16 h = (__bf16)x;
   return __builtin_bit_cast(uint16_t, h);
@@ -49,12 +62,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
-  return (a & 0xFFFFu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xFFFF0000u);
-}
 
 // Work items are (sequence x KV head, row tile, split) with the split fastest.
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
@@ -68,13 +75,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
     const uint64_t* __restrict__ anc, const int* __restrict__ n_nodes, int N, int Hq, int Hkv,
     int cap, int S, int KS, int MT, int items, float scale_log2, float* __restrict__ Opart,
     float* __restrict__ Mpart, float* __restrict__ Lpart, int batch) {
-  constexpr int KP = D + 8;          // K tile pitch (bf16): 16-byte reads spread over banks
-  constexpr int VP = kTileKeys + 4;  // V^T tile pitch (bf16)
-  constexpr int KCH = D / 8;         // 16-byte chunks per key row
-  constexpr int KLD = kTileKeys * KCH / kAttnThreads;       // K chunks per thread
-  constexpr int VGROUPS = (kTileKeys / 4) * KCH;            // (4 keys x 8 d) groups
+  constexpr int KP = D + 8;   // K tile pitch (bf16): 16-byte reads spread over banks
+  constexpr int VP = D + 16;  // V tile pitch (bf16): the 16 rows of a transposing read
+                              // (4 keys x 4 column groups) fall in distinct banks
+  constexpr int KCH = D / 8;  // 16-byte chunks per key row
+  constexpr int KLD = kTileKeys * KCH / kAttnThreads;  // K (and V) chunks per thread
   __shared__ __align__(16) uint16_t Ks[kTileKeys * KP];
-  __shared__ __align__(16) uint16_t Vt[D * VP];
+  __shared__ __align__(16) uint16_t Vs[kTileKeys * VP];
   __shared__ uint64_t Aw[kAttnWaves * 32 * 16];  // ancestor rows (tree split)
 
   const int w = blockIdx.x;
@@ -134,59 +141,65 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
   const uint16_t* kbase = kc + ((int64_t)b * Hkv + g) * (int64_t)cap * D;
   const uint16_t* vbase = vc + ((int64_t)b * Hkv + g) * (int64_t)cap * D;
 
-  // register prefetch of one tile: K chunks and one (4 keys x 8 d) V group.
-  // Rows past the tile's end are clamped to the last valid row (always in
-  // bounds, no branch) and zeroed when staged.
-  uint4 kreg[KLD];
-  uint4 vreg[4];
+  // register prefetch of one tile: 16-byte K and V chunks, row-major, by
+  // buffer loads over this head's cache rows (the tile start in the scalar
+  // offset, the thread's chunk in a fixed vector offset).  Rows of the last,
+  // partial tile past its end are clamped to its last row (always in
+  // bounds) and zeroed when staged.
+  const uint32_t head_bytes = (uint32_t)cap * D * 2u;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, head_bytes, 0x00020000);
+  uint4 kreg[KLD], vreg[KLD];
   auto fetch = [&](int kt) {
-    const int last = k1 - 1;
+    if (kt + kTileKeys <= k1) {  // whole tile
+      const uint32_t soff = (uint32_t)kt * D * 2u;
 #pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int c = tid + i * kAttnThreads;
-      const int key = min(kt + c / KCH, last), col = (c % KCH) * 8;
-      kreg[i] = *reinterpret_cast<const uint4*>(kbase + (int64_t)key * D + col);
-    }
-    {
-      // every thread loads a V group (duplicates past VGROUPS are not
-      // staged) so the number of loads in flight is the same in every lane
-      const int gi = tid % VGROUPS;
-      const int kq = gi % (kTileKeys / 4), col = (gi / (kTileKeys / 4)) * 8;
+      for (int i = 0; i < KLD; ++i) {
+        const int c = tid + i * kAttnThreads;
+        const uint32_t voff = (uint32_t)((c / KCH) * D + (c % KCH) * 8) * 2u;
+        kreg[i] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       krs, voff, soff, 0));
+        vreg[i] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       vrs, voff, soff, 0));
+      }
+    } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = min(kt + 4 * kq + r, last);
-        vreg[r] = *reinterpret_cast<const uint4*>(vbase + (int64_t)key * D + col);
+      for (int i = 0; i < KLD; ++i) {
+        const int c = tid + i * kAttnThreads;
+        const uint32_t voff = (uint32_t)(min(kt + c / KCH, k1 - 1) * D + (c % KCH) * 8) * 2u;
+        kreg[i] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       krs, voff, 0, 0));
+        vreg[i] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       vrs, voff, 0, 0));
       }
     }
   };
   auto stage = [&](int kt) {
+    const bool whole = kt + kTileKeys <= k1;
 #pragma unroll
     for (int i = 0; i < KLD; ++i) {
       const int c = tid + i * kAttnThreads;
       const int key = c / KCH, col = (c % KCH) * 8;
-      *reinterpret_cast<uint4*>(&Ks[key * KP + col]) =
-          kt + key < k1 ? kreg[i] : make_uint4(0, 0, 0, 0);
-    }
-    if (tid < VGROUPS) {
-      // lanes with consecutive tid hold consecutive 4-key groups of the same
-      // 8 d's: each 16-lane group writes one contiguous 128-byte V^T row
-      const int kq = tid % (kTileKeys / 4), col = (tid / (kTileKeys / 4)) * 8;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (kt + 4 * kq + r >= k1) vreg[r] = make_uint4(0, 0, 0, 0);
-      const uint32_t a[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-      const uint32_t bq[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-      const uint32_t cq[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
-      const uint32_t dq[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint2 ev = make_uint2(lo_halves(a[j], bq[j]), lo_halves(cq[j], dq[j]));
-        uint2 od = make_uint2(hi_halves(a[j], bq[j]), hi_halves(cq[j], dq[j]));
-        *reinterpret_cast<uint2*>(&Vt[(col + 2 * j) * VP + 4 * kq]) = ev;
-        *reinterpret_cast<uint2*>(&Vt[(col + 2 * j + 1) * VP + 4 * kq]) = od;
+      uint4 kv = kreg[i], vv = vreg[i];
+      if (!whole && kt + key >= k1) {  // rows past the end stage as zeros
+        kv = make_uint4(0, 0, 0, 0);
+        vv = kv;
       }
+      *reinterpret_cast<uint4*>(&Ks[key * KP + col]) = kv;
+      *reinterpret_cast<uint4*>(&Vs[key * VP + col]) = vv;
     }
   };
+  // transposing-read source of this lane: key offset 4 (lane / 32) +
+  // (lane % 16) / 4 and column offset 16 ((lane / 16) % 2) + 4 (lane % 4)
+  // inside each (16 keys x 32 d) block of the A operand
+  const int tr_key = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   // The tree split keeps each row's ancestor words in LDS, so the tile loop
   // issues no global load other than the K/V prefetch: waiting for any other
@@ -200,21 +213,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
   for (int kt = k0; kt < k1; kt += kTileKeys) {
     stage(kt);
     lds_barrier();
-    fetch(min(kt + kTileKeys, k1 - 1));  // in flight during the products
-    const uint64_t aword = split == S ? aw[(kt - L) >> 6] : 0ull;  // kt - L: multiple of 64
+    if (kt + kTileKeys < k1) fetch(kt + kTileKeys);  // in flight during the products
 
     if (wave_active) {
       // visibility of the 64 keys, taken before the matrix products so that
       // their results are consumed in straight-line code.  valid bit j =
       // key kt + j exists for this row; the lane's 32 keys are nibbles
       // 0, 2, ..., 14 of (valid >> 4 * half) (the S^T accumulator layout).
-      uint64_t valid = split == S ? (row_ok ? aword : 0ull) : (row_ok ? ~0ull : 0ull);
-      if (k1 - kt < 64) valid &= (1ull << (k1 - kt)) - 1ull;
-      uint64_t v = (valid >> (4 * half)) & 0x0F0F0F0F0F0F0F0Full;
-      v = (v | (v >> 4)) & 0x00FF00FF00FF00FFull;
-      v = (v | (v >> 8)) & 0x0000FFFF0000FFFFull;
-      v = (v | (v >> 16)) & 0x00000000FFFFFFFFull;
-      const uint32_t vis = (uint32_t)v;
+      // A whole context tile needs no mask when every row of the wave is live.
+      uint32_t vis = row_ok ? 0xFFFFFFFFu : 0u;
+      if (split == S || kt + kTileKeys > k1) {
+        uint64_t valid = split == S ? (row_ok ? aw[(kt - L) >> 6] : 0ull) : (row_ok ? ~0ull : 0ull);
+        if (k1 - kt < 64) valid &= (1ull << (k1 - kt)) - 1ull;
+        uint64_t v = (valid >> (4 * half)) & 0x0F0F0F0F0F0F0F0Full;
+        v = (v | (v >> 4)) & 0x00FF00FF00FF00FFull;
+        v = (v | (v >> 8)) & 0x0000FFFF0000FFFFull;
+        v = (v | (v >> 16)) & 0x00000000FFFFFFFFull;
+        vis = (uint32_t)v;
+      }
       const bool full = __ballot(vis != 0xFFFFFFFFu) == 0;  // wave-uniform
 
       // S^T = K Q^T for the two 32-key sub-tiles
@@ -280,12 +296,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
           bf16x8 bp;
 #pragma unroll
           for (int j = 0; j < 8; ++j) bp[j] = (__bf16)p[16 * ks + 8 * t + j];
+          const int rr = 32 * ks + 16 * t + tr_key;  // key rows rr and rr + 8
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const uint16_t* vrow = &Vt[(32 * db + l32) * VP + 32 * ks + 16 * t + 4 * half];
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-            const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            // A = V^T: d = 32 db + lane % 32; k-slots 0..3 and 4..7 of the lane
+            // are keys 16 t + 4 half + {0..3} and 16 t + 8 + 4 half + {0..3}
+            const uint16_t* vsrc = &Vs[rr * VP + 32 * db + tr_col];
+            const s16x4 lo = lds_read_tr16(vsrc);
+            const s16x4 hi = lds_read_tr16(vsrc + 8 * VP);
+            const bf16x8 a =
+                __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp, oacc[db], 0, 0, 0);
           }
         }
