@@ -9,12 +9,17 @@ independent sets (>= 1 GiB) that every step reads HBM, not the 256 MB
 Infinity Cache.
 
 Prints ONE JSON line (rank 0).  `value` = tree node x query-head rows
-verified per second (rounds/s x N x Hq).  `roofline` is for the kernel(s) of
-the dominant call, from HIP events recorded around every call on the stream
-the call runs on.  `cpu_baseline` times the CPU oracle on a bounded sample
-of the same workload.
+verified per second (rounds/s x N x Hq).  `roofline` is for the verification
+pass, tv_tree_attention_verify (kernels k_attn_partial + k_attn_combine),
+from HIP events recorded around every call on the stream the call runs on;
+its `traffic` comes from the HBM byte counters recorded in
+profiles/attention_<workload>_traffic.md when that record was taken on the
+current attention source (else null).  `cpu_baseline` times the CPU oracle
+on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 500] [--warmup 50] [--workload 4b]
+    python bench.py --copy-calibration      # a plain device copy of known size,
+                                            # the reference for the byte counters
 """
 import argparse
 import json
@@ -41,7 +46,49 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="replay each round from a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run 20 plain 256 MiB device-to-device copies and exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """20 launches of a plain copy of 256 MiB: FETCH_SIZE / WRITE_SIZE of this
+    kernel divided by 256 MiB give the counters' scale factor."""
+    import torch
+    x = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda")
+    x.fill_(1)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(20):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": x.numel(), "launches": 20}), flush=True)
+
+
+def source_digest(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per tv_tree_attention_verify call from the committed counter
+    record, if it was taken on the current attention source."""
+    rec = os.path.join(ROOT, "profiles", f"attention_{workload}_traffic.md")
+    src = os.path.join(ROOT, "tree_verification_best_amd", "csrc", "tv_attention.hip")
+    if not os.path.exists(rec):
+        return None
+    vals = {}
+    for line in open(rec):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256_16") != source_digest(src):
+        return None
+    try:
+        return int(vals["hbm_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
 
 
 def algorithmic_bytes(c, b, N, Lsum, build):
@@ -86,7 +133,8 @@ def cpu_baseline(c, sets0, seconds):
                 parent, token, depth, anc, nn = (tr["parent"], tr["token"], tr["depth"],
                                                  tr["anc"], tr["n_nodes"])
             else:
-                parent, token, depth, anc, nn = c["_tree"]
+                parent, token, depth, nn = c["_tree"]
+                anc = np.stack([oracle.ancestors(parent[s])[0] for s in range(b)])
             oracle.tree_attention(q, k, v, ctx, anc, nn)
             oracle.tree_accept(target, parent, token, depth, nn, mode=mode,
                                temperature=max(c["_T"], 1e-3), seed=1234, round=rounds,
@@ -100,6 +148,9 @@ def cpu_baseline(c, sets0, seconds):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the path has no multi-GPU mode (run with --gpus 1)",
               file=sys.stderr)
@@ -136,9 +187,7 @@ def main():
         parent, token, depth = workloads.random_trees(c, b, N, max_depth=K,
                                                       max_children=c.get("max_children", 4))
         nn = np.full(b, N, np.int32)
-        import oracle  # only to lay out the fixed random trees' ancestor rows for the CPU leg
-        anc = np.stack([oracle.ancestors(parent[s])[0] for s in range(b)])
-        c["_tree"] = (parent, token, depth, anc, nn)
+        c["_tree"] = (parent, token, depth, nn)
         first = (first[0], workloads.plant(first[1], parent, token, nn, 9.0)) + first[2:]
         tree_in = [torch.from_numpy(a).to(dev) for a in (parent, token, nn)]
 
@@ -154,7 +203,7 @@ def main():
     for i in range(1, nsets):
         s = make_set(i)
         if not c["build"]:
-            s = (s[0], workloads.plant(s[1], *c["_tree"][:2], c["_tree"][4], 9.0)) + s[2:]
+            s = (s[0], workloads.plant(s[1], *c["_tree"][:2], c["_tree"][3], 9.0)) + s[2:]
         sets.append(to_dev(s))
     ctx0 = first[6]
     max_ctx = int(ctx0.max())
@@ -272,16 +321,24 @@ def main():
         tf = aflops / (calls["attention"] * 1e-3) / 1e12
         per_call["attention"]["TFLOPs"] = round(tf, 2)
         per_call["attention"]["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
-    if calls:
-        dom = max(calls, key=lambda k: calls[k])
-        kernels = {"build": "k_chunk_topk+k_chunk_z+k_finalize+k_select",
-                   "attention": "k_attn_partial+k_attn_combine",
-                   "accept": "k_rowmax+k_rowz+k_walk"}
-        gbs = abytes[dom] / (calls[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "call": "tv_tree_" + dom,
-                "kernels": kernels[dom], "ms": round(calls[dom], 5),
-                "algorithmic_bytes": abytes[dom]}
+    if "attention" in calls:
+        # the verification pass: HBM-bound below the ridge point, else MFMA
+        ms = calls["attention"]
+        ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        intensity = aflops / abytes["attention"]
+        traffic = recorded_traffic(args.workload)
+        if intensity < ridge:
+            gbs = abytes["attention"] / (ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        else:
+            tf = aflops / (ms * 1e-3) / 1e12
+            roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        roof.update({"traffic": traffic, "call": "tv_tree_attention_verify",
+                     "kernels": "k_attn_partial+k_attn_combine", "ms": round(ms, 5),
+                     "algorithmic_bytes": abytes["attention"], "algorithmic_flops": aflops,
+                     "intensity_flop_per_byte": round(intensity, 1)})
 
     cpu = None
     if not args.no_cpu_baseline:
