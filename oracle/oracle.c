@@ -652,7 +652,9 @@ static int accept_one(const float *target, const float *draft, int N, int K, int
         double qt = (t >= 0 && t < V) ? (double)Wq[t] / (double)Zq : 0.0;
         draw(seed, round, seq, (uint64_t)u, 0, rnd);
         double u53 = (double)(rnd[0] >> 11) * 0x1p-53;
-        int accept = (pt >= qt) || (u53 < pt / qt);
+        /* min(1, p/q): p = 0 (including a token outside the vocabulary)
+         * gives probability 0, whatever q is */
+        int accept = pt > 0.0 && ((pt >= qt) || (u53 < pt / qt));
         if (accept) {
             acc_nodes[++len] = c;
             out_tokens[len - 1] = t;

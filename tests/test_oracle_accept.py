@@ -337,6 +337,25 @@ def test_draft_proposal_rejects_branching_tree(orc):
     assert res["accept_len"][0] == -1
 
 
+def test_draft_proposal_zero_target_mass_never_accepted(orc):
+    """min(1, p/q) is 0 where p is 0: a child whose token the target gives no
+    mass (a -inf logit, or a token outside the vocabulary) is rejected on
+    every draw, even where q is 0 too; where q is 0 and p is not, the child
+    is accepted on every draw."""
+    V, b = 8, 400
+    p_l = np.linspace(-1.0, 1.0, V).astype(np.float32)
+    q_l = p_l.copy()
+    p_l[3] = -np.inf          # p(3) = 0, q(3) > 0
+    p_l[5] = q_l[5] = -np.inf  # p(5) = q(5) = 0
+    q_l[6] = -np.inf          # q(6) = 0 < p(6)
+    for y, expect in ((3, 0), (5, 0), (-2, 0), (V + 1, 0), (6, 1)):
+        res = _draft_chain_trials(orc, p_l, q_l, 0, np.full(b, y))
+        assert np.all(res["accept_len"] == expect), (y, expect)
+        if expect == 0:  # the residual never emits a token of zero target mass
+            first = res["out_tokens"][:, 0]
+            assert np.all((first >= 0) & (first < V) & (first != 3) & (first != 5))
+
+
 def test_sampled_is_replayable(orc):
     """Same (seed, round) -> same draws; another round -> other draws."""
     r = np.random.default_rng(42)
