@@ -204,8 +204,8 @@ tv_status tv_tree_attention_verify(const void *q, const void *k_cache, const voi
  * counter (round, b, u, i); the final draw at node u uses words 0 and 1 of
  * counter (round, b, u, 0xFFFFFFFF) as a 128-bit uniform and an exact
  * integer inverse CDF over the weights.  POINT_MASS accepts iff
- * U * Z_res < W(t) * 2^64 (exact).  DRAFT accepts iff p >= q or
- * (U >> 11) * 2^-53 < p / q in fp64, and its residual weights are
+ * U * Z_res < W(t) * 2^64 (exact).  DRAFT accepts iff p > 0 and (p >= q
+ * or (U >> 11) * 2^-53 < p / q) in fp64, and its residual weights are
  * rint(max(0, p - q) * 2^62).
  *
  *   target_logits [batch][N][V]   dtype dt; row i = the target's next-token
@@ -220,7 +220,7 @@ tv_status tv_tree_attention_verify(const void *q, const void *k_cache, const voi
  * A node at depth max_depth is treated as a leaf.  Tokens outside [0, V)
  * are never accepted.
  * Limits: V <= 2^18; N <= 1024; 1 <= max_depth <= 1023; temperature > 0 in
- * sampled mode; K >= 1 with draft_logits in DRAFT mode.
+ * sampled mode; 1 <= K <= 64 with draft_logits in DRAFT mode.
  * ------------------------------------------------------------------------ */
 size_t tv_tree_accept_workspace(int batch, int N, int K, int V, tv_accept_mode mode,
                                 tv_proposal proposal);

@@ -137,6 +137,81 @@ def test_accept_draft_proposal_chain(V):
     assert int(g["accept_len"][0]) == -1
 
 
+@pytest.mark.parametrize("mode", ["greedy", "sampled"])
+def test_accept_wide_star_and_full_rows(mode):
+    """A root with 150 children (three groups of wave lanes, tokens repeated
+    across groups) and a 1024-row tree (most final draws derived on demand)."""
+    r = np.random.default_rng(51)
+    V = 700
+    # star: root + 150 children, then one grandchild under each of 5 children
+    N1 = 156
+    parent = np.full((3, N1), 0, np.int32)
+    parent[:, 0] = -1
+    parent[:, 151:] = np.arange(1, 6)
+    depth = np.where(np.arange(N1) == 0, 0, np.where(np.arange(N1) > 150, 2, 1))
+    depth = np.tile(depth.astype(np.int32), (3, 1))
+    token = r.integers(0, 40, size=(3, N1)).astype(np.int32)  # many repeats
+    token[1, 70] = token[1, 3]
+    target = (r.standard_normal((3, N1, V)) * 1.2).astype(np.float32)
+    target[:, 0, :40] += 3.0  # the children's tokens carry most of the root's mass
+    n = np.array([N1, N1, 100], np.int32)
+    m = oracle.GREEDY if mode == "greedy" else oracle.SAMPLED
+    for rnd in range(4):
+        g, o = _both(target, parent, token, depth, n, mode=m, max_depth=3, seed=21, round=rnd)
+        assert_accept_equal(g, o, f"star round {rnd}")
+    # 1024 rows
+    N2 = 1024
+    parent, token, depth, n = _random_trees(r, 2, N2, 300, max_children=3, ns=[N2, 777])
+    target = (r.standard_normal((2, N2, 300)) * 1.5).astype(np.float32)
+    target = workloads.plant(target, parent, token, n, 6.0)
+    for rnd in range(3):
+        g, o = _both(target, parent, token, depth, n, mode=m, max_depth=int(depth.max()) + 1,
+                     seed=8, round=rnd)
+        assert_accept_equal(g, o, f"1024 rows round {rnd}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_accept_draft_proposal_edge_tokens(dtype):
+    """DRAFT chains with tokens of zero target mass, tokens outside the
+    vocabulary, a bad depth on an unvisited and on a visited node, and the
+    largest drafter depth (K = 64)."""
+    r = np.random.default_rng(61)
+    b, K, V = 24, 64, 5000
+    N = K + 1
+    target = (r.standard_normal((b, N, V)) * 1.0).astype(np.float32)
+    draft = (target[:, :K] + 0.2 * r.standard_normal((b, K, V))).astype(np.float32)
+    parent = np.tile(np.arange(-1, N - 1, dtype=np.int32), (b, 1))
+    depth = np.tile(np.arange(N, dtype=np.int32), (b, 1))
+    token = np.zeros((b, N), np.int32)
+    for s in range(b):
+        for j in range(K):
+            token[s, j + 1] = int(np.argmax(draft[s, j]))  # likely accepted for a while
+    target[0, 0, token[0, 1]] = -np.inf    # p = 0 at the first child
+    token[1, 1] = -3                      # outside the vocabulary
+    token[2, 1] = V + 7
+    token[3, 2] = token[3, 1]
+    target[3, 1, token[3, 2]] = -np.inf
+    depth[4, 3] = 0                       # bad depth, visited only if 2 levels accept
+    depth[5, 1] = K + 5                   # bad depth on the first child
+    n = np.array([N - (s % 5) for s in range(b)], np.int32)
+    for rnd in range(3):
+        g, o = _both(target, parent, token, depth, n, mode=oracle.SAMPLED, dtype=dtype,
+                     draft=draft, proposal=oracle.DRAFT, seed=13, round=rnd, max_depth=K)
+        assert_accept_equal(g, o, f"draft edges round {rnd}")
+    assert int(g["accept_len"][5]) == -1
+    assert int(g["accept_len"][1]) == 0 and int(g["accept_len"][2]) == 0
+
+
+def test_accept_draft_proposal_limits():
+    t = torch.zeros((1, 2, 16), device="cuda")
+    d = torch.zeros((1, 65, 16), device="cuda")
+    i = torch.zeros((1, 2), dtype=torch.int32, device="cuda")
+    n = torch.ones(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(tv.TreeVerifyError):
+        tv.tv_tree_accept(t, i, i, i, n, mode=tv.TV_SAMPLED, max_depth=1,
+                          proposal=tv.TV_PROPOSAL_DRAFT, draft_logits=d)
+
+
 def test_accept_replayable():
     r = np.random.default_rng(4)
     parent, token, depth, n = _random_trees(r, 4, 40, 2000)

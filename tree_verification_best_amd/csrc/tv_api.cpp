@@ -154,6 +154,7 @@ tv_status tv_tree_accept(const void* target_logits, const void* draft_logits, tv
   const bool draft = sampled && proposal == TV_PROPOSAL_DRAFT;
   if (sampled && !finite_pos(temperature)) return TV_ERR_INVALID;
   if (draft && (!draft_logits || K < 1)) return TV_ERR_INVALID;
+  if (draft && K > TV_MAX_POSITIONS) return TV_ERR_UNSUPPORTED;
   if (batch < 1 || N < 1 || V < 1 || max_depth < 1) return TV_ERR_INVALID;
   if (!accept_args_ok(batch, N, V, max_depth)) return TV_ERR_UNSUPPORTED;
   const tvk::AcceptPlan p = tvk::accept_plan(batch, N, K, V, sampled, draft);

@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
       float tmax = -__builtin_inff();
 #pragma unroll
       for (int i = 0; i < 32; i += 2) tmax = fmaxf(tmax, fmaxf(x[i], x[i + 1]));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = fmaxf(tmax, xor32_f(tmax));
       const bool grow = tmax > m_run;
       if (__ballot(grow)) {
         const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - tmax) * scale_log2) : 1.f;
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
   // loop body, a different basic block: wait out the result latency before
   // the stores read them.
   __builtin_amdgcn_s_sleep(2);
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = l_run + xor32_f(l_run);
   if (row_ok) {
     const int64_t pr = (((int64_t)split * batch + b) * N + node) * Hq + h;
     if (half == 0) {

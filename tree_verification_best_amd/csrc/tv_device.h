@@ -182,41 +182,68 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
   return __builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, v), l));
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
-  uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int d) {
-  uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)v, d);
-  uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(v >> 32), d);
-  return ((uint64_t)hi << 32) | lo;
+// the value held by lane (lane ^ 32): the gfx950 lane-swap instruction swaps
+// the upper half of the first operand with the lower half of the second
+__device__ __forceinline__ float xor32_f(float v) {
+  const uint32_t x = __builtin_bit_cast(uint32_t, v);
+  const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return __builtin_bit_cast(float, (uint32_t)((lane_id() & 32) ? p[0] : p[1]));
 }
 
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 1; m < WAVE; m <<= 1) v += shfl_xor_u64(v, m);
-  return v;
+// ---------------------------------------------------------------------------
+// Wave scans and reductions by DPP: row shifts (within rows of 16 lanes)
+// then row broadcasts (lane 15 into the next row, lane 31 into rows 2 and 3),
+// the standard inclusive-scan pattern; a lane without a source reads the
+// operation's identity.  Reductions read the total from lane 63.  All 64
+// lanes must be active.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_or(uint32_t identity, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = dpp_or<CTRL, ROWS>(0u, (uint32_t)v);
+  const uint32_t hi = dpp_or<CTRL, ROWS>(0u, (uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
 }
 // inclusive prefix sum over lanes
 __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int d = 1; d < WAVE; d <<= 1) {
-    uint64_t o = shfl_up_u64(v, d);
-    if (l >= d) v += o;
-  }
+  v += dpp_u64<0x111, 0xF>(v);
+  v += dpp_u64<0x112, 0xF>(v);
+  v += dpp_u64<0x114, 0xF>(v);
+  v += dpp_u64<0x118, 0xF>(v);
+  v += dpp_u64<0x142, 0xA>(v);
+  v += dpp_u64<0x143, 0xC>(v);
   return v;
+}
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+  return readlane_u64(wave_incl_scan_u64(v), WAVE - 1);
 }
 __device__ __forceinline__ int wave_incl_scan_i(int v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int d = 1; d < WAVE; d <<= 1) {
-    int o = __shfl_up(v, d);
-    if (l >= d) v += o;
-  }
+  v += (int)dpp_or<0x111, 0xF>(0u, (uint32_t)v);
+  v += (int)dpp_or<0x112, 0xF>(0u, (uint32_t)v);
+  v += (int)dpp_or<0x114, 0xF>(0u, (uint32_t)v);
+  v += (int)dpp_or<0x118, 0xF>(0u, (uint32_t)v);
+  v += (int)dpp_or<0x142, 0xA>(0u, (uint32_t)v);
+  v += (int)dpp_or<0x143, 0xC>(0u, (uint32_t)v);
   return v;
 }
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  const uint32_t ninf = 0xFF800000u;
+  return fmaxf(v, __builtin_bit_cast(float, dpp_or<CTRL, ROWS>(ninf, __builtin_bit_cast(uint32_t, v))));
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = dpp_max_step<0x111, 0xF>(v);
+  v = dpp_max_step<0x112, 0xF>(v);
+  v = dpp_max_step<0x114, 0xF>(v);
+  v = dpp_max_step<0x118, 0xF>(v);
+  v = dpp_max_step<0x142, 0xA>(v);
+  v = dpp_max_step<0x143, 0xC>(v);
+  return readlane_f(v, WAVE - 1);
+}
+
 // Inclusive scans over the wave by DPP row shifts (within rows of 16 lanes)
 // and row broadcasts (lane 15 into the next row, lane 31 into rows 2 and 3);
 // lanes with no source read 0.  For non-negative ints (sum and max).
@@ -242,11 +269,6 @@ __device__ __forceinline__ int wave_scan_max_dpp(int v) {
   v = max(v, dpp_i<0x143, 0xC>(v));
   return v;
 }
-__device__ __forceinline__ float wave_max_f(float v) {
-#pragma unroll
-  for (int m = 1; m < WAVE; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
-}
 
 // ---------------------------------------------------------------------------
 // (value, id) order used by top-k and argmax: larger value first, then the
@@ -257,16 +279,26 @@ __device__ __forceinline__ bool vi_better(float av, int ai, float bv, int bi) {
 }
 
 // Argmax over a wave of (value, id) pairs in the order above.
-__device__ __forceinline__ void wave_argmax(float& v, int& id) {
-#pragma unroll
-  for (int m = 1; m < WAVE; m <<= 1) {
-    float ov = __shfl_xor(v, m);
-    int oi = __shfl_xor(id, m);
-    if (vi_better(ov, oi, v, id)) {
-      v = ov;
-      id = oi;
-    }
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void dpp_argmax_step(float& v, int& id) {
+  const float ov = __builtin_bit_cast(
+      float, dpp_or<CTRL, ROWS>(0xFF800000u, __builtin_bit_cast(uint32_t, v)));
+  const int oi = (int)dpp_or<CTRL, ROWS>(0x7FFFFFFFu, (uint32_t)id);
+  if (vi_better(ov, oi, v, id)) {
+    v = ov;
+    id = oi;
   }
+}
+// the wave's best (value, id) in every lane
+__device__ __forceinline__ void wave_argmax(float& v, int& id) {
+  dpp_argmax_step<0x111, 0xF>(v, id);
+  dpp_argmax_step<0x112, 0xF>(v, id);
+  dpp_argmax_step<0x114, 0xF>(v, id);
+  dpp_argmax_step<0x118, 0xF>(v, id);
+  dpp_argmax_step<0x142, 0xA>(v, id);
+  dpp_argmax_step<0x143, 0xC>(v, id);
+  v = readlane_f(v, WAVE - 1);
+  id = readlane_i(id, WAVE - 1);
 }
 
 // ---------------------------------------------------------------------------

@@ -62,7 +62,9 @@ struct AcceptPlan {
   int chunk, C;
   int64_t rows;  // batch * N target rows (+ batch * K draft rows in DRAFT mode)
   bool draft_rows;
-  size_t off_cmax, off_carg, off_cz;
+  // chunk records, chunk-major ([C][rows]); segment sums [rows][C][16]; DRAFT
+  // residual chunk sums [batch][64] and the per-sequence hand-over record
+  size_t off_cmax, off_carg, off_cz, off_cseg, off_rcz, off_pend;
   size_t workspace;
 };
 
