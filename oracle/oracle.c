@@ -172,7 +172,9 @@ void tvo_philox4x64_10(const uint64_t ctr_in[4], const uint64_t key_in[2], uint6
 }
 
 /* One draw of the acceptance walk: key = (seed, 0),
- * counter = (round, sequence, node, slot). */
+ * counter = (round, sequence, node, slot).  Each node owns two draws: the
+ * uniform that decides its own acceptance (slot ACCEPT_SLOT) and the one
+ * behind the final draw made at it (slot RESIDUAL_SLOT). */
 static void draw(uint64_t seed, uint64_t round, uint64_t seq, uint64_t node, uint64_t slot,
                  uint64_t out[4])
 {
@@ -181,6 +183,7 @@ static void draw(uint64_t seed, uint64_t round, uint64_t seq, uint64_t node, uin
     tvo_philox4x64_10(ctr, key, out);
 }
 
+#define ACCEPT_SLOT 0ULL
 #define RESIDUAL_SLOT 0xFFFFFFFFULL
 
 /* ------------------------------------------------------------------------- */
@@ -617,7 +620,7 @@ static int accept_one(const float *target, const float *draft, int N, int K, int
             for (int i = 0; i < nk; ++i) {
                 int t = token[kids[i]];
                 uint64_t w = (t >= 0 && t < V && !excl[t]) ? W[t] : 0;
-                draw(seed, round, seq, (uint64_t)u, (uint64_t)i, rnd);
+                draw(seed, round, seq, (uint64_t)kids[i], ACCEPT_SLOT, rnd);
                 u128 lhs = (u128)rnd[0] * Zres;         /* U * Z_res        */
                 u128 rhs = (u128)w << 64;               /* W[t] * 2^64      */
                 if (lhs < rhs) { next = kids[i]; break; }
@@ -650,7 +653,7 @@ static int accept_one(const float *target, const float *draft, int N, int K, int
         uint64_t Zq = tvo_row_weights(qrow, V, inv_t, Wq);
         double pt = (t >= 0 && t < V) ? (double)W[t] / (double)Z : 0.0;
         double qt = (t >= 0 && t < V) ? (double)Wq[t] / (double)Zq : 0.0;
-        draw(seed, round, seq, (uint64_t)u, 0, rnd);
+        draw(seed, round, seq, (uint64_t)c, ACCEPT_SLOT, rnd);
         double u53 = (double)(rnd[0] >> 11) * 0x1p-53;
         /* min(1, p/q): p = 0 (including a token outside the vocabulary)
          * gives probability 0, whatever q is */
@@ -691,7 +694,9 @@ static int accept_one(const float *target, const float *draft, int N, int K, int
 /* Acceptance for a batch: target [b][N][V]; draft [b][K][V] (DRAFT only);
  * parent/token/depth [b][N]; n_nodes [b]; accept_len [b];
  * accepted_nodes / out_tokens [b][max_depth + 1].
- * Sequence b uses Philox counters (round, b, node, slot). */
+ * Sequence b uses Philox counters (round, b, node, slot): node c's
+ * acceptance uses (round, b, c, 0), the final draw at node u uses
+ * (round, b, u, 0xFFFFFFFF). */
 int tvo_tree_accept(const float *target, const float *draft, int batch, int N, int K, int V,
                     const int32_t *parent, const int32_t *token, const int32_t *depth,
                     const int32_t *n_nodes, int mode, float temperature, int proposal,

@@ -356,6 +356,53 @@ def test_draft_proposal_zero_target_mass_never_accepted(orc):
             assert np.all((first >= 0) & (first < V) & (first != 3) & (first != 5))
 
 
+def test_draws_are_keyed_by_the_deciding_node(orc):
+    """Pin of the draw layout, written from the Philox words alone: child c
+    of the root is accepted iff U_c * Z_res < W(t_c) * 2^64 with U_c = word 0
+    of counter (round, b, c, 0) under key (seed, 0), Z_res the root's mass
+    minus the tokens already rejected; after both children are rejected the
+    emitted token is the smallest v whose running residual mass exceeds
+    floor(U * Z_res / 2^128), U = words 0, 1 of (round, b, 0, 0xFFFFFFFF)."""
+    r = np.random.default_rng(44)
+    V, b, rnd = 12, 3, 7
+    row = (r.standard_normal(V) * 0.8).astype(np.float32)
+    W, Z = orc.row_weights(row)
+    W = [int(w) for w in W]
+    t1, t2 = 4, 9
+    target = np.broadcast_to(row, (b, 3, V))
+    parent = np.broadcast_to(np.array([-1, 0, 0], np.int32), (b, 3))
+    token = np.broadcast_to(np.array([0, t1, t2], np.int32), (b, 3))
+    depth = np.broadcast_to(np.array([0, 1, 1], np.int32), (b, 3))
+    seen = set()
+    for seed in range(60):
+        res = orc.tree_accept(target, parent, token, depth, np.full(b, 3, np.int32),
+                              mode=orc.SAMPLED, seed=seed, round=rnd, max_depth=1)
+        for s in range(b):
+            key = [seed, 0]
+            u1 = int(orc.philox([rnd, s, 1, 0], key)[0])
+            u2 = int(orc.philox([rnd, s, 2, 0], key)[0])
+            if u1 * Z < W[t1] << 64:
+                want = (1, t1)
+            elif u2 * (Z - W[t1]) < W[t2] << 64:
+                want = (1, t2)
+            else:
+                f = orc.philox([rnd, s, 0, 0xFFFFFFFF], key)
+                U = (int(f[0]) << 64) | int(f[1])
+                zres = Z - W[t1] - W[t2]
+                R = (U * zres) >> 128
+                run, tok = 0, None
+                for v in range(V):
+                    run += 0 if v in (t1, t2) else W[v]
+                    if run > R:
+                        tok = v
+                        break
+                want = (0, tok)
+            got = (int(res["accept_len"][s]), int(res["out_tokens"][s, 0]))
+            assert got == want, (seed, s, got, want)
+            seen.add(want[0] if want[0] == 0 else want[1])
+    assert seen == {0, t1, t2}  # every branch of the rule was exercised
+
+
 def test_sampled_is_replayable(orc):
     """Same (seed, round) -> same draws; another round -> other draws."""
     r = np.random.default_rng(42)
