@@ -200,10 +200,10 @@ tv_status tv_tree_attention_verify(const void *q, const void *k_cache, const voi
  *     A node with more than one child sets accept_len[b] = -1.
  * The round emits the accepted drafts and one more token.
  *
- * Draws: acceptance of the i-th child of node u uses Philox word 0 of
- * counter (round, b, u, i); the final draw at node u uses words 0 and 1 of
- * counter (round, b, u, 0xFFFFFFFF) as a 128-bit uniform and an exact
- * integer inverse CDF over the weights.  POINT_MASS accepts iff
+ * Draws: the acceptance of node c uses Philox word 0 of counter
+ * (round, b, c, 0) under key (seed, 0); the final draw at node u uses words
+ * 0 and 1 of counter (round, b, u, 0xFFFFFFFF) as a 128-bit uniform and an
+ * exact integer inverse CDF over the weights.  POINT_MASS accepts iff
  * U * Z_res < W(t) * 2^64 (exact).  DRAFT accepts iff p > 0 and (p >= q
  * or (U >> 11) * 2^-53 < p / q) in fp64, and its residual weights are
  * rint(max(0, p - q) * 2^62).

@@ -11,14 +11,15 @@
 //   k_rowmax       grid (chunks, rows)  (max, argmax) of each 4096-token chunk
 //                                       of every target row (and draft row in
 //                                       DRAFT mode), stored chunk-major
-//   k_rowz         grid (chunks, rows)  fixed-point softmax mass of each chunk
-//                                       and of its sixteen 256-token segments
-//                                       (sampled modes)
-//   k_walk         grid (batch)         four waves gather the tree, the row
-//                                       statistics, the children's weights and
-//                                       every Philox draw into LDS; one wave
-//                                       then walks the tree and makes the final
-//                                       draw chunk -> segment -> token
+//   k_rowz         grid (chunks, rows)  fixed-point softmax mass of each chunk,
+//                                       and the weight of each child's token
+//                                       that falls in the chunk (sampled modes)
+//   k_walk         grid (batch)         gathers the tree, the row statistics,
+//                                       the children's weights and every Philox
+//                                       draw into LDS, decides every node in
+//                                       parallel, follows the decisions from the
+//                                       root and makes the final draw (chunk,
+//                                       then token within the chunk)
 //   k_draft_resid  grid (chunks, batch) DRAFT rejection: chunk sums of the
 //                                       residual (p - q)+ of the rejected node
 //   k_draft_pick   grid (batch)         DRAFT rejection: the residual draw
@@ -33,8 +34,6 @@ namespace tvk {
 
 constexpr int kAccNT = 256;
 constexpr int kAccE = kAcceptChunk / kAccNT;  // 16 tokens per thread and chunk
-constexpr int kSeg = 256;                     // tokens per segment of the final draw
-constexpr int kSegs = kAcceptChunk / kSeg;    // 16 segments per chunk
 constexpr int kMaxN = 1024;                   // rows per sequence
 constexpr int kMaxDraftRows = 64;             // drafter positions (DRAFT proposal)
 constexpr int kMaxChunks = 64;                // chunks per row (V <= 2^18)
@@ -109,36 +108,6 @@ struct ChunkLoad<uint16_t> {
   }
 };
 
-// four consecutive tokens [v0, v0 + 4) of a row; -inf past the end
-template <typename T>
-__device__ __forceinline__ void load4(const T* p, int v0, int V, float (&x)[4]);
-template <>
-__device__ __forceinline__ void load4(const float* p, int v0, int V, float (&x)[4]) {
-  if (v0 + 4 <= V && (V & 3) == 0) {
-    const float4 a = *reinterpret_cast<const float4*>(p + v0);
-    x[0] = a.x;
-    x[1] = a.y;
-    x[2] = a.z;
-    x[3] = a.w;
-  } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) x[q] = v0 + q < V ? p[v0 + q] : -__builtin_inff();
-  }
-}
-template <>
-__device__ __forceinline__ void load4(const uint16_t* p, int v0, int V, float (&x)[4]) {
-  if (v0 + 4 <= V && (V & 3) == 0) {
-    const uint2 a = *reinterpret_cast<const uint2*>(p + v0);
-    x[0] = __builtin_bit_cast(float, a.x << 16);
-    x[1] = __builtin_bit_cast(float, a.x & 0xFFFF0000u);
-    x[2] = __builtin_bit_cast(float, a.y << 16);
-    x[3] = __builtin_bit_cast(float, a.y & 0xFFFF0000u);
-  } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) x[q] = v0 + q < V ? bf16_to_f32(p[v0 + q]) : -__builtin_inff();
-  }
-}
-
 // (max, argmax lowest id) of each 4096-token chunk of every row, stored at
 // [chunk][row].  Rows past n_nodes are read too (they are inside the array)
 // and never used.  Without ARG only the maximum is kept.
@@ -193,17 +162,25 @@ __global__ __launch_bounds__(kAccNT) void k_rowmax(const T* __restrict__ target,
   }
 }
 
-// Fixed-point softmax mass of each chunk (at [chunk][row]) and of each of its
-// 256-token segments (at [row][chunk][segment]).  The chunk's logits are
-// loaded first; the row maximum (from the chunk maxima) arrives while they
-// are in flight.  A segment is the 16 lanes of one DPP row.
+// Fixed-point softmax mass of each chunk, at [chunk][row].  The chunk's
+// logits are loaded first; the row maximum (from the chunk maxima) arrives
+// while they are in flight.
+// With the tree given (wtg non-null), the block also stores the weight of
+// every child's token that falls in its chunk: wtg[b][x] = W of token(x) in
+// the row of parent(x); in DRAFT mode (wqg non-null) a draft row's block
+// stores wqg[b][x] = W of token(x) in draft row depth(x) - 1.
 template <typename T>
 __global__ __launch_bounds__(kAccNT) void k_rowz(const T* __restrict__ target,
                                                 const T* __restrict__ draft, int V, int C,
                                                 int64_t trows, int64_t rows, float inv_t,
                                                 const float* __restrict__ cmax,
-                                                uint64_t* __restrict__ cz,
-                                                uint64_t* __restrict__ cseg) {
+                                                uint64_t* __restrict__ cz, int N, int K,
+                                                const int* __restrict__ parent,
+                                                const int* __restrict__ token,
+                                                const int* __restrict__ depth,
+                                                const int* __restrict__ n_nodes,
+                                                uint64_t* __restrict__ wtg,
+                                                uint64_t* __restrict__ wqg) {
   __shared__ float s_m;
   __shared__ uint64_t wsum[kAccNT / WAVE];
   const int c = blockIdx.x;
@@ -224,16 +201,29 @@ __global__ __launch_bounds__(kAccNT) void k_rowz(const T* __restrict__ target,
   uint64_t acc = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) acc += weight(x[j], m, inv_t);  // -inf padding weighs 0
-  // inclusive sums within each row of 16 lanes: lane 15 of a row holds the
-  // mass of its segment
-  acc += dpp_u64<0x111, 0xF>(acc);
-  acc += dpp_u64<0x112, 0xF>(acc);
-  acc += dpp_u64<0x114, 0xF>(acc);
-  acc += dpp_u64<0x118, 0xF>(acc);
-  if ((lane & 15) == 15) cseg[((int64_t)r * C + c) * kSegs + threadIdx.x / 16] = acc;
-  const uint64_t wt = readlane_u64(acc, 15) + readlane_u64(acc, 31) + readlane_u64(acc, 47) +
-                      readlane_u64(acc, 63);
-  if (lane == 0) wsum[threadIdx.x / WAVE] = wt;
+  acc = wave_sum_u64(acc);
+  if (lane == 0) wsum[threadIdx.x / WAVE] = acc;
+  if (wtg) {
+    // children whose tokens fall in this chunk (the logit is re-read: the
+    // block has just brought the chunk into the cache)
+    const bool trow = r < trows;
+    if (trow || wqg) {
+      const int64_t j = trow ? r : r - trows;
+      const int bb = (int)(j / (trow ? N : K));
+      const int uu = (int)(j - (int64_t)bb * (trow ? N : K));
+      const int nn = n_nodes[bb];
+      const int64_t o = (int64_t)bb * N;
+      if (nn >= 1 && nn <= N && (!trow || uu < nn)) {
+        for (int xx = 1 + (int)threadIdx.x; xx < nn; xx += kAccNT) {
+          const bool mine = trow ? parent[o + xx] == uu : depth[o + xx] == uu + 1;
+          if (!mine) continue;
+          const int t = token[o + xx];
+          if (t >= base && t < base + kAcceptChunk && t < V)
+            (trow ? wtg : wqg)[o + xx] = weight(Elem<T>::load(p, t), m, inv_t);
+        }
+      }
+    }
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     uint64_t z = 0;
@@ -252,41 +242,43 @@ struct DraftPending {
   uint64_t zu, zq, d0, d1;
 };
 
-// A child's acceptance weight with its token, packed for the exclusion
-// passes: bit 63 = token inside the vocabulary, bits 18..62 = weight
-// (at most 2^44), bits 0..17 = token.
-__device__ __forceinline__ uint64_t pack_excl(bool valid, uint64_t w, int t) {
-  return valid ? (1ull << 63) | (w << 18) | (uint64_t)(uint32_t)t : 0ull;
-}
-__device__ __forceinline__ bool excl_valid(uint64_t e) { return (e >> 63) != 0; }
-__device__ __forceinline__ uint64_t excl_w(uint64_t e) { return (e >> 18) & ((1ull << 45) - 1); }
-__device__ __forceinline__ int excl_t(uint64_t e) { return (int)(e & 0x3FFFFu); }
+// Decision at each node, filled before the walk: the child the walk moves
+// to (>= 0), or one of these codes.
+constexpr int kNextNone = 0x7fffffff;  // no child accepted (or no child): final draw here
+constexpr int kNextErr = -2;           // DRAFT: more than one child, or a bad depth
+__device__ __forceinline__ int draft_reject_code(int c) { return -3 - c; }  // DRAFT rejection of c
 
 struct WalkShared {
-  int par[kMaxN], tkn[kMaxN];
-  int off[kMaxN + 1];  // children per node, then their offsets (CSR, row order)
-  int kids[kMaxN];     // gather: owner of each CSR entry; walk: children of u
-  float rmax[kMaxN];   // row maximum
+  int par[kMaxN], tkn[kMaxN];  // par[] holds the excluded tokens during the final draw
+  int off[kMaxN + 1];          // children per node, then CSR offsets
+  uint32_t list[kMaxN];        // children in CSR order: node | valid << 10 | token << 11
+  uint64_t kexl[kMaxN];        // children in CSR order: node | effective weight << 10
+  int next[kMaxN];             // decision at each node
+  float rmax[kMaxN];           // row maximum
   union {
-    int rarg[kMaxN];  // greedy: row argmax, lowest id on ties
-    struct {
-      uint64_t rz[kMaxN];    // row mass Z
-      uint64_t wc[kMaxN];    // weight of node c's token in its parent's row
-      uint64_t draw[kMaxN];  // word 0 of the acceptance draw of each CSR entry
-    } s;
-  } u;
-  union {
-    uint64_t kex[kMaxN];  // point mass: packed (token, effective weight) of u's children
-    double qt[kMaxN];     // DRAFT: q of node c's token at its depth (NaN: depth outside [1, K])
-  } v;
-  uint64_t rd0[kAccNT], rd1[kAccNT];  // final draws of nodes < nres
+    int rarg[kMaxN];     // greedy: row argmax, lowest id on ties
+    uint64_t rz[kMaxN];  // sampled: row mass Z
+  } r;
+  uint64_t adraw[kMaxN];              // word 0 of each node's acceptance draw
+  uint64_t rd0[kAccNT], rd1[kAccNT];  // final draws of nodes < 256
   float pmax[kAccNT];                 // per-part row statistics
   int parg[kAccNT];
-  uint64_t pz[kAccNT];
+  uint64_t pz[kAccNT];  // then the thread sums of the final draw
   float dmax[kMaxDraftRows];
   uint64_t dz[kMaxDraftRows];
+  uint64_t czsub[kMaxChunks];  // rejected children's mass per chunk (final draw)
   int wtot[kAccNT / WAVE];
+  int wfirst[kAccNT / WAVE];
+  int cs, tok;
+  uint64_t r2;
 };
+
+__device__ __forceinline__ uint32_t pack_sib(int x, bool valid, int t) {
+  return (uint32_t)x | (valid ? 1u << 10 : 0u) | (valid ? (uint32_t)t << 11 : 0u);
+}
+__device__ __forceinline__ int sib_node(uint32_t e) { return (int)(e & 1023u); }
+__device__ __forceinline__ bool sib_valid(uint32_t e) { return (e >> 10) & 1u; }
+__device__ __forceinline__ int sib_tok(uint32_t e) { return (int)(e >> 11); }
 
 // floor((hi 2^64 + lo) * Z / 2^128), exact
 __device__ __forceinline__ uint64_t scaled_draw(uint64_t hi, uint64_t lo, uint64_t Z) {
@@ -296,6 +288,72 @@ __device__ __forceinline__ uint64_t scaled_draw(uint64_t hi, uint64_t lo, uint64
   return h1 + (s0 < h0 ? 1ull : 0ull);
 }
 
+// Smallest token of chunk `base` whose running sum exceeds R, given the 16
+// consecutive weights of each thread (thread t: tokens base + 16t ...).
+// Whole block; every thread returns the token (0x7fffffff if none).  The
+// thread sums are monotone in thread order, so the token lies in the first
+// thread whose inclusive sum exceeds R: found by ballots, not by atomics
+// (a same-address LDS atomic from many lanes is serialised lane by lane).
+__device__ int block_pick(const uint64_t (&w)[16], int base, uint64_t R, uint64_t* tsum,
+                          int* wfirst, int* tok) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
+  uint64_t run = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) run += w[j];
+  tsum[tid] = run;
+  __syncthreads();
+  if (tid < WAVE) {
+    const uint64_t a0 = tsum[4 * tid], a1 = tsum[4 * tid + 1], a2 = tsum[4 * tid + 2],
+                   a3 = tsum[4 * tid + 3];
+    const uint64_t s4 = a0 + a1 + a2 + a3;
+    uint64_t ex = wave_incl_scan_u64(s4) - s4;
+    tsum[4 * tid] = ex;
+    ex += a0;
+    tsum[4 * tid + 1] = ex;
+    ex += a1;
+    tsum[4 * tid + 2] = ex;
+    ex += a2;
+    tsum[4 * tid + 3] = ex;
+  }
+  __syncthreads();
+  const uint64_t ex = tsum[tid];
+  const uint64_t bal = __ballot(ex + run > R);
+  if (lane == 0) wfirst[wave] = bal ? __ffsll((unsigned long long)bal) - 1 : WAVE;
+  __syncthreads();
+  int first = -1;
+  for (int w2 = 0; w2 < kAccNT / WAVE; ++w2) {
+    const int f = wfirst[w2];
+    if (f < WAVE) {
+      first = w2 * WAVE + f;
+      break;
+    }
+  }
+  if (first < 0) return 0x7fffffff;
+  if (tid == first) {
+    uint64_t acc = ex;
+    int jj = 15;
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      acc += w[j];
+      if (!found && acc > R) {
+        jj = j;
+        found = true;
+      }
+    }
+    *tok = base + 16 * tid + jj;
+  }
+  __syncthreads();
+  return *tok;
+}
+
+// The acceptance of a child depends only on its parent's row and on its
+// earlier siblings, never on the path that reaches the parent: with
+// Z_res(c) = Z_p - (mass of the distinct tokens of the siblings before c),
+// child c of p passes iff U(c) * Z_res(c) < W_eff(c) * 2^64, where
+// W_eff(c) = 0 for a token an earlier sibling already carries.  So every
+// decision is made in parallel before the walk, and the walk follows next[]
+// from the root.
 template <typename T, int MODE>
 __global__ __launch_bounds__(kAccNT) void k_walk(
     const T* __restrict__ target, const T* __restrict__ draft, int N, int K, int V, int C,
@@ -303,8 +361,8 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
     const int* __restrict__ depth, const int* __restrict__ n_nodes, float inv_t,
     uint64_t seed, uint64_t round, int max_depth, const float* __restrict__ cmax,
     const int* __restrict__ carg, const uint64_t* __restrict__ cz,
-    const uint64_t* __restrict__ cseg, int64_t trows, int64_t rows,
-    int* __restrict__ accept_len, int* __restrict__ accepted_nodes,
+    const uint64_t* __restrict__ wtg, const uint64_t* __restrict__ wqg, int64_t trows,
+    int64_t rows, int* __restrict__ accept_len, int* __restrict__ accepted_nodes,
     int* __restrict__ out_tokens, DraftPending* __restrict__ pend) {
   constexpr bool kSampled = MODE != kGreedy;
   __shared__ WalkShared sh;
@@ -314,67 +372,107 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
   const int64_t rb = (int64_t)b * N;
   int* acc_nodes = accepted_nodes + (int64_t)b * width;
   int* out_tok = out_tokens + (int64_t)b * width;
+
+  // ---- 1. every load that needs nothing but the shapes, issued together:
+  // the tree and the children's weights (thread t owns nodes t + 256 k, all
+  // N rows are inside the arrays), the first batch of row statistics, and
+  // n_nodes.  Rows (all N of the sequence, then its K draft rows in DRAFT
+  // mode) are split into P parts of the chunk list so that every thread has
+  // work; lanes of a part hold consecutive rows, so each chunk-major load is
+  // coalesced.
+  int pv[4], tv[4], dv[4];
+  uint64_t wv[4], qv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = tid + k * kAccNT;
+    const int64_t at = rb + (c < N ? c : 0);
+    pv[k] = parent[at];
+    tv[k] = token[at];
+    dv[k] = MODE == kDraft ? depth[at] : 0;
+    wv[k] = kSampled ? wtg[at] : 0ull;
+    qv[k] = MODE == kDraft ? wqg[at] : 0ull;
+  }
+  const int nr = N + (MODE == kDraft ? K : 0);
+  const int P = min(C, max(1, kAccNT / nr));
+  const int RP = kAccNT / P;
+  const int part = tid / RP, rr = tid - part * RP;
+  float mv[16];
+  int av[16];
+  uint64_t zv[16];
+  // a batch of 16 chunks of row pass r0 (addresses clamped inside the arrays
+  // for idle threads and past the last chunk)
+  auto load_batch = [&](int r0, int j0) {
+    const int r = r0 + rr;
+    const bool act = part < P && r < nr;
+    const int64_t grow = !act ? 0 : (r < N ? rb + r : trows + (int64_t)b * K + (r - N));
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int j = j0 + q * P;
+      const int64_t at = (int64_t)(j < C ? j : 0) * rows + grow;
+      mv[q] = cmax[at];
+      if (!kSampled) av[q] = carg[at];
+      else zv[q] = cz[at];
+    }
+  };
+  load_batch(0, part);
+  const int n = n_nodes[b];
   for (int j = tid; j < width; j += kAccNT) {
     acc_nodes[j] = -1;
     out_tok[j] = -1;
   }
   if (MODE == kDraft && tid == 0) pend[b].flag = 0;
-  const int n = n_nodes[b];
   if (n < 1 || n > N) {
     if (tid == 0) accept_len[b] = -1;
     return;
   }
-
-  // ---- 1. the tree (kept in registers until the statistics are in) and the
-  // row statistics: rows are split into P parts of the chunk list so that
-  // every thread has work; lanes of a part hold consecutive rows, so each
-  // chunk-major load is coalesced
-  int pv[4], tv[4], dv[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int c = tid + k * kAccNT;
-    const int64_t at = rb + (c < n ? c : 0);
-    pv[k] = parent[at];
-    tv[k] = token[at];
-    dv[k] = MODE == kDraft ? depth[at] : 0;
-    if (c >= n) pv[k] = tv[k] = -1;
-  }
   for (int j = tid; j <= n; j += kAccNT) sh.off[j] = 0;
-  const int nr = n + (MODE == kDraft ? K : 0);
-  const int P = min(C, max(1, kAccNT / nr));
-  const int RP = kAccNT / P;
-  const int part = tid / RP, rr = tid - part * RP;
+  for (int j = tid; j < n; j += kAccNT) sh.next[j] = kNextNone;
+
+  // every draw: acceptance draws of nodes 1..n-1, then final draws of
+  // nodes < 256
+  auto make_draws = [&]() {
+    const int na = n - 1, nf = min(n, kAccNT);
+    for (int jj = tid; jj < na + nf; jj += kAccNT) {
+      const bool accd = jj < na;
+      const int node = accd ? jj + 1 : jj - na;
+      const u64x4 d = philox4x64_10(round, (uint64_t)b, (uint64_t)node,
+                                    accd ? 0ull : kResidualSlot, seed, 0);
+      if (accd) {
+        sh.adraw[node] = d.v[0];
+      } else {
+        sh.rd0[node] = d.v[0];
+        sh.rd1[node] = d.v[1];
+      }
+    }
+  };
   for (int r0 = 0; r0 < nr; r0 += RP) {
     const int r = r0 + rr;
     const bool act = part < P && r < nr;
-    const int64_t grow = !act ? 0 : (r < n ? rb + r : trows + (int64_t)b * K + (r - n));
     float m = -__builtin_inff();
     int a = 0x7fffffff;
     uint64_t z = 0;
-    for (int j0 = part; act && j0 < C; j0 += 16 * P) {
-      float mv[16];
-      int av[16];
-      uint64_t zv[16];
+    auto reduce_batch = [&](int j0) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int j = j0 + q * P;
-        const int64_t at = (int64_t)(j < C ? j : 0) * rows + grow;
-        mv[q] = cmax[at];
-        if (!kSampled) av[q] = carg[at];
-        else zv[q] = cz[at];
-      }
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        if (j0 + q * P >= C) break;
+        const bool in = j0 + q * P < C;  // no early exit: the loads stay batched
         if (!kSampled) {
-          if (vi_better(mv[q], av[q], m, a)) {
+          if (in && vi_better(mv[q], av[q], m, a)) {
             m = mv[q];
             a = av[q];
           }
         } else {
-          m = fmaxf(m, mv[q]);
-          z += zv[q];
+          m = fmaxf(m, in ? mv[q] : -__builtin_inff());
+          z += in ? zv[q] : 0ull;
         }
+      }
+    };
+    if (r0 > 0) load_batch(r0, part);
+    if (kSampled && r0 == 0) make_draws();  // while the first loads are in flight
+    if (act) {
+      reduce_batch(part);
+      for (int j0 = part + 16 * P; j0 < C; j0 += 16 * P) {
+        load_batch(r0, j0);
+        reduce_batch(j0);
       }
     }
     if (part < P) {
@@ -400,46 +498,44 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
           bz += sh.pz[i];
         }
       }
-      if (rw < n) {
+      if (rw < N) {
         sh.rmax[rw] = bm;
-        if (!kSampled) sh.u.rarg[rw] = ba;
-        else sh.u.s.rz[rw] = bz;
+        if (!kSampled) sh.r.rarg[rw] = ba;
+        else sh.r.rz[rw] = bz;
       } else {
-        sh.dmax[rw - n] = bm;
-        sh.dz[rw - n] = bz;
+        sh.dmax[rw - N] = bm;
+        sh.dz[rw - N] = bz;
       }
     }
     __syncthreads();
   }
 
-  // ---- 2. tree into LDS, children counted, logits of the children's tokens
-  float lt[4], lq[4];
+  // ---- 2. tree into LDS; children counted (the returned count is the
+  // child's place in its parent's list)
+  bool child[4], okt[4];
+  int pos[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int c = tid + k * kAccNT;
+    if (c >= n) pv[k] = tv[k] = -1;
     if (c < n) {
       sh.par[c] = pv[k];
       sh.tkn[c] = tv[k];
     }
-    const bool child = c >= 1 && c < n && pv[k] >= 0 && pv[k] < n;
-    if (kSampled && child) atomicAdd(&sh.off[pv[k]], 1);
-    const bool okt = child && tv[k] >= 0 && tv[k] < V;
-    lt[k] = 0.f;
-    lq[k] = 0.f;
-    if (kSampled) {
-      lt[k] = Elem<T>::load(target + (rb + (okt ? pv[k] : 0)) * (int64_t)V, okt ? tv[k] : 0);
-      if (MODE == kDraft) {
-        const bool okq = okt && dv[k] >= 1 && dv[k] <= K;
-        lq[k] = Elem<T>::load(draft + ((int64_t)b * K + (okq ? dv[k] - 1 : 0)) * (int64_t)V,
-                              okq ? tv[k] : 0);
-      }
-    }
+    child[k] = c >= 1 && c < n && pv[k] >= 0 && pv[k] < n;
+    okt[k] = child[k] && tv[k] >= 0 && tv[k] < V;
+    pos[k] = (kSampled && child[k]) ? atomicAdd(&sh.off[pv[k]], 1) : 0;
   }
   __syncthreads();
 
-  if (kSampled) {
-    // ---- 3. CSR offsets of the children (exclusive scan of the counts) and
-    // the acceptance weights
+  if (MODE == kGreedy) {
+    // the first child in row order whose token is the row's argmax
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (child[k] && tv[k] == sh.r.rarg[pv[k]]) atomicMin(&sh.next[pv[k]], tid + k * kAccNT);
+    __syncthreads();
+  } else {
+    // ---- 3. CSR offsets: exclusive scan of the counts
     int a4[4];
     int s = 0;
 #pragma unroll
@@ -450,21 +546,6 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
     }
     const int incl = wave_incl_scan_i(s);
     if (lane == WAVE - 1) sh.wtot[wave] = incl;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int c = tid + k * kAccNT;
-      if (c >= n) continue;
-      const bool child = c >= 1 && pv[k] >= 0 && pv[k] < n;
-      const bool okt = child && tv[k] >= 0 && tv[k] < V;
-      sh.u.s.wc[c] = okt ? weight(lt[k], sh.rmax[pv[k]], inv_t) : 0ull;
-      if (MODE == kDraft) {
-        double q = __builtin_nan("");
-        if (dv[k] >= 1 && dv[k] <= K)
-          q = okt ? (double)weight(lq[k], sh.dmax[dv[k] - 1], inv_t) / (double)sh.dz[dv[k] - 1]
-                  : 0.0;
-        sh.v.qt[c] = q;
-      }
-    }
     __syncthreads();
     int ex = incl - s;
     for (int w = 0; w < wave; ++w) ex += sh.wtot[w];
@@ -476,280 +557,202 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
     }
     if (tid == 0) sh.off[n] = sh.wtot[0] + sh.wtot[1] + sh.wtot[2] + sh.wtot[3];
     __syncthreads();
-
-    // ---- 4. every draw the walk can use: the acceptance draw of each
-    // (node, child slot) entry, then the final draw of as many nodes as the
-    // idle threads of the last pass can take
-    for (int u = tid; u < n; u += kAccNT) {
-      const int o1 = sh.off[u + 1];
-      for (int i = sh.off[u]; i < o1; ++i) sh.kids[i] = u;
+    int slot[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      slot[k] = child[k] ? sh.off[pv[k]] + pos[k] : 0;
+      if (child[k]) sh.list[slot[k]] = pack_sib(tid + k * kAccNT, okt[k], tv[k]);
     }
     __syncthreads();
-  }
-  const int E = kSampled ? sh.off[n] : 0;
-  const int slots = max(1, (E + kAccNT - 1) / kAccNT) * kAccNT;
-  const int nres = kSampled ? min(n, slots - E) : 0;
-  if (kSampled) {
-    for (int j = tid; j < slots; j += kAccNT) {
-      const bool accd = j < E;
-      const int uu = accd ? sh.kids[j] : j - E;
-      if (accd || uu < n) {
-        const uint64_t slot = accd ? (uint64_t)(j - sh.off[uu]) : kResidualSlot;
-        const u64x4 d = philox4x64_10(round, (uint64_t)b, (uint64_t)uu, slot, seed, 0);
-        if (accd) {
-          sh.u.s.draw[j] = d.v[0];
+
+    // ---- 4. per child: whether an earlier sibling carries the same token,
+    // and its effective weight; DRAFT: the decision at the parent
+    uint64_t wef[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = tid + k * kAccNT;
+      wef[k] = 0;
+      if (!child[k]) continue;
+      const int p = pv[k], t = tv[k];
+      const int o0 = sh.off[p], o1 = sh.off[p + 1];
+      const uint64_t w = okt[k] ? wv[k] : 0ull;
+      if (MODE == kPointMass) {
+        bool dup = false;
+        for (int e0 = o0; e0 < o1; e0 += 8) {
+          uint32_t sb[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) sb[q] = sh.list[min(e0 + q, o1 - 1)];
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            dup |= sib_node(sb[q]) < c && sib_valid(sb[q]) && sib_tok(sb[q]) == t;
+        }
+        wef[k] = dup ? 0ull : w;
+        sh.kexl[slot[k]] = (uint64_t)c | (wef[k] << 10);
+      } else {
+        // DRAFT: p(t) and q(t); a chain node has one child
+        if (o1 - o0 > 1 || dv[k] < 1 || dv[k] > K) {
+          sh.next[p] = kNextErr;
         } else {
-          sh.rd0[uu] = d.v[0];
-          sh.rd1[uu] = d.v[1];
+          const double pt = okt[k] ? (double)w / (double)sh.r.rz[p] : 0.0;
+          const double qt = okt[k] ? (double)qv[k] / (double)sh.dz[dv[k] - 1] : 0.0;
+          const double u53 = (double)(sh.adraw[c] >> 11) * 0x1p-53;
+          // min(1, p/q): a token the target gives no mass is never accepted
+          const bool ok = pt > 0.0 && (pt >= qt || u53 < pt / qt);
+          sh.next[p] = ok ? c : draft_reject_code(c);
         }
       }
     }
     __syncthreads();
+
+    if (MODE == kPointMass) {
+      // ---- 5. per child: the residual mass it is tested against
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c = tid + k * kAccNT;
+        if (!child[k]) continue;
+        const int p = pv[k];
+        const int o0 = sh.off[p], o1 = sh.off[p + 1];
+        uint64_t before = 0;
+        for (int e0 = o0; e0 < o1; e0 += 8) {
+          uint64_t kb[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) kb[q] = sh.kexl[min(e0 + q, o1 - 1)];
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (e0 + q < o1 && (int)(kb[q] & 1023u) < c) before += kb[q] >> 10;
+        }
+        const uint64_t zres = sh.r.rz[p] - before;
+        if (__umul64hi(sh.adraw[c], zres) < wef[k]) atomicMin(&sh.next[p], c);
+      }
+      __syncthreads();
+    }
   }
 
-  // ---- the walk: one wave, LDS only except the final draw
-  if (wave != 0) return;
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
-
-  // children of u in row order into sh.kids[0..nk)
-  auto list_children = [&](int u, int nk) {
-    int found = 0;
-    for (int base = 1; found < nk && base < n; base += 4 * WAVE) {
-      int pq[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = base + q * WAVE + lane;
-        pq[q] = sh.par[c < n ? c : 0];
-        if (c >= n) pq[q] = -1;
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bool is = pq[q] == u;
-        const uint64_t bal = __ballot(is);
-        if (is) sh.kids[found + __popcll(bal & lt_mask)] = base + q * WAVE + lane;
-        found += __popcll(bal);
-      }
+  // ---- the walk: every wave follows next[] from the root (LDS reads only)
+  if (tid == 0) acc_nodes[0] = 0;
+  int u = 0, len = 0, nx = kNextNone;
+  for (;;) {
+    nx = len < max_depth ? sh.next[u] : kNextNone;
+    if (nx < 0 || nx == kNextNone) break;
+    ++len;
+    if (tid == 0) {
+      acc_nodes[len] = nx;
+      out_tok[len - 1] = sh.tkn[nx];
     }
-    wave_lds_sync();
-  };
-  // f(packed child) for each of the nk children of u, in order (uniform)
-  auto for_each_excl = [&](int nk, auto&& f) {
-    for (int g = 0; g < nk; g += WAVE) {
-      const uint64_t e = sh.v.kex[g + (g + lane < nk ? lane : 0)];
-      const int m = min(WAVE, nk - g);
-      for (int j = 0; j < m; ++j) f(readlane_u64(e, j));
-    }
-  };
-  // Final draw at u from the target row with the children's tokens removed:
-  // chunk, then 256-token segment, then token, each by a wave scan of exact
-  // integer sums.  czu: lane j holds the mass of chunk j of row u.
-  auto final_draw = [&](int u, uint64_t Z, int nk, uint64_t czu) -> int {
-    uint64_t d0, d1;
-    if (u < nres) {
-      d0 = sh.rd0[u];
-      d1 = sh.rd1[u];
-    } else {
-      const u64x4 d = philox4x64_10(round, (uint64_t)b, (uint64_t)u, kResidualSlot, seed, 0);
-      d0 = d.v[0];
-      d1 = d.v[1];
-    }
-    const uint64_t R = scaled_draw(d0, d1, Z);
-    uint64_t cw = lane < C ? czu : 0ull;
-    for_each_excl(nk, [&](uint64_t e) {
-      if (excl_valid(e) && (excl_t(e) >> 12) == lane) cw -= excl_w(e);
-    });
-    const uint64_t incl = wave_incl_scan_u64(cw);
-    const uint64_t hit = __ballot(lane < C && incl > R);
-    if (!hit) return -1;
-    const int cs = __ffsll((unsigned long long)hit) - 1;
-    const uint64_t R2 = R - readlane_u64(incl - cw, cs);
-    uint64_t sw = cseg[((rb + u) * C + cs) * kSegs + (lane < kSegs ? lane : 0)];
-    if (lane >= kSegs) sw = 0;
-    for_each_excl(nk, [&](uint64_t e) {
-      const int t = excl_t(e);
-      if (excl_valid(e) && (t >> 12) == cs && ((t >> 8) & (kSegs - 1)) == lane) sw -= excl_w(e);
-    });
-    const uint64_t incl2 = wave_incl_scan_u64(sw);
-    const uint64_t hit2 = __ballot(lane < kSegs && incl2 > R2);
-    if (!hit2) return -1;
-    const int ss = __ffsll((unsigned long long)hit2) - 1;
-    const uint64_t R3 = R2 - readlane_u64(incl2 - sw, ss);
-    const int v0 = cs * kAcceptChunk + ss * kSeg + 4 * lane;
-    float x[4];
-    load4(target + (rb + u) * (int64_t)V, v0, V, x);
-    const float m = sh.rmax[u];
-    uint64_t w4[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) w4[q] = weight(x[q], m, inv_t);
-    for_each_excl(nk, [&](uint64_t e) {
-      const int t = excl_t(e);
-      if (excl_valid(e)) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (t == v0 + q) w4[q] = 0;
-      }
-    });
-    const uint64_t s4 = w4[0] + w4[1] + w4[2] + w4[3];
-    const uint64_t incl3 = wave_incl_scan_u64(s4);
-    const uint64_t hit3 = __ballot(incl3 > R3);
-    if (!hit3) return -1;
-    const int L = __ffsll((unsigned long long)hit3) - 1;
-    uint64_t run = incl3 - s4;
-    int tok = v0 + 3;
-#pragma unroll
-    for (int q = 3; q >= 0; --q) {
-      // smallest q with run + w4[0..q] > R3
-      uint64_t pre = run;
-      for (int k = 0; k <= q; ++k) pre += w4[k];
-      if (pre > R3) tok = v0 + q;
-    }
-    return readlane_i(tok, L);
-  };
-
-  if (lane == 0) acc_nodes[0] = 0;
-  int u = 0, len = 0, bonus = -1;
+    u = nx;
+  }
+  int bonus = -1;
   bool err = false, pending = false;
   if (MODE == kGreedy) {
-    for (;;) {
-      const int a = sh.u.rarg[u];
-      int nxt = -1;
-      if (len < max_depth) {
-        for (int base = 1; base < n && nxt < 0; base += 4 * WAVE) {
-          int pq[4], tq[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int c = base + q * WAVE + lane;
-            pq[q] = sh.par[c < n ? c : 0];
-            tq[q] = sh.tkn[c < n ? c : 0];
-            if (c >= n) pq[q] = -1;
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint64_t bal = __ballot(pq[q] == u && tq[q] == a);
-            if (bal && nxt < 0) nxt = base + q * WAVE + __ffsll((unsigned long long)bal) - 1;
-          }
-        }
+    bonus = sh.r.rarg[u];
+  } else if (MODE == kDraft && nx == kNextErr) {
+    err = true;
+  } else if (MODE == kDraft && nx != kNextNone) {
+    // rejection of child c: the residual (p - q)+ is drawn by the kernels
+    // that follow
+    const int c = -3 - nx;
+    if (tid == 0) {
+      const int dd = depth[rb + c];
+      DraftPending pd;
+      pd.flag = 1;
+      pd.u = u;
+      pd.dd = dd;
+      pd.len = len;
+      pd.mu = sh.rmax[u];
+      pd.mq = sh.dmax[dd - 1];
+      pd.zu = sh.r.rz[u];
+      pd.zq = sh.dz[dd - 1];
+      if (u < kAccNT) {
+        pd.d0 = sh.rd0[u];
+        pd.d1 = sh.rd1[u];
+      } else {
+        const u64x4 dr = philox4x64_10(round, (uint64_t)b, (uint64_t)u, kResidualSlot, seed, 0);
+        pd.d0 = dr.v[0];
+        pd.d1 = dr.v[1];
       }
-      if (nxt < 0) {
-        bonus = a;
-        break;
-      }
-      ++len;
-      if (lane == 0) {
-        acc_nodes[len] = nxt;
-        out_tok[len - 1] = a;
-      }
-      u = nxt;
+      pend[b] = pd;
     }
-  } else if (MODE == kPointMass) {
-    for (;;) {
-      // chunk masses of row u, for the final draw if every child is rejected
-      const uint64_t czu = cz[(int64_t)(lane < C ? lane : 0) * rows + rb + u];
-      const int o = sh.off[u];
-      const int nk = len < max_depth ? sh.off[u + 1] - o : 0;
-      uint64_t Zres = sh.u.s.rz[u];
-      int nxt = -1;
-      if (nk > 0) {
-        list_children(u, nk);
-        for (int g = 0; g < nk && nxt < 0; g += WAVE) {
-          const int i = g + lane;
-          const bool live = i < nk;
-          const int c = sh.kids[live ? i : 0];
-          const int t = sh.tkn[c];
-          const uint64_t w0 = sh.u.s.wc[c];
-          const uint64_t d = sh.u.s.draw[o + (live ? i : 0)];
-          // a token already tried by an earlier child weighs nothing
-          bool dup = false;
-          const int m = min(WAVE, nk - g);
-          for (int j = 0; j < m - 1; ++j) dup |= (j < lane) && (readlane_i(t, j) == t);
-          for (int j = 0; j < g; ++j) dup |= excl_valid(sh.v.kex[j]) && excl_t(sh.v.kex[j]) == t;
-          const bool okt = t >= 0 && t < V;
-          const uint64_t w = (live && !dup) ? w0 : 0ull;
-          if (live) sh.v.kex[i] = pack_excl(okt, w, t);
-          const uint64_t incl = wave_incl_scan_u64(w);
-          const uint64_t zres = Zres - (incl - w);
-          const bool ok = live && (__umul64hi(d, zres) < w);
-          const uint64_t bal = __ballot(ok);
-          if (bal) nxt = readlane_i(c, __ffsll((unsigned long long)bal) - 1);
-          Zres -= readlane_u64(incl, WAVE - 1);
+    pending = true;
+  } else {
+    // ---- final draw at u from the target row with u's children removed
+    // (none past the depth limit, and none in DRAFT mode where u is a leaf):
+    // wave 0 picks the chunk from the exact chunk masses, then the block
+    // weighs that chunk's 4096 tokens and picks the token.
+    const int64_t grow = rb + u;
+    const int o0 = sh.off[u];
+    const int nk = (MODE == kPointMass && len < max_depth) ? sh.off[u + 1] - o0 : 0;
+    if (wave == 0) {
+      const int jl = lane < C ? lane : 0;
+      const uint64_t czu = cz[(int64_t)jl * rows + grow];
+      uint64_t d0, d1;
+      if (u < kAccNT) {
+        d0 = sh.rd0[u];
+        d1 = sh.rd1[u];
+      } else {
+        const u64x4 d = philox4x64_10(round, (uint64_t)b, (uint64_t)u, kResidualSlot, seed, 0);
+        d0 = d.v[0];
+        d1 = d.v[1];
+      }
+      // the rejected children's mass, per chunk (an LDS histogram) and in
+      // total; their tokens go to par[] for the token-level exclusion
+      sh.czsub[lane] = 0;
+      wave_lds_sync();
+      uint64_t zx = 0;
+      for (int g = 0; g < nk; g += WAVE) {
+        const int i = g + lane;
+        if (i < nk) {
+          const uint32_t sb = sh.list[o0 + i];
+          const uint64_t we = sh.kexl[o0 + i] >> 10;
+          sh.par[i] = sib_valid(sb) ? sib_tok(sb) : -1;
+          if (we) atomicAdd((unsigned long long*)&sh.czsub[sib_tok(sb) >> 12],
+                            (unsigned long long)we);
+          zx += we;
         }
-        wave_lds_sync();
       }
-      if (nxt >= 0) {
-        ++len;
-        if (lane == 0) {
-          acc_nodes[len] = nxt;
-          out_tok[len - 1] = sh.tkn[nxt];
-        }
-        u = nxt;
-        continue;
-      }
-      bonus = final_draw(u, Zres, nk, czu);
-      break;
-    }
-  } else {  // DRAFT proposal: chains only
-    for (;;) {
-      const uint64_t czu = cz[(int64_t)(lane < C ? lane : 0) * rows + rb + u];
-      const int o = sh.off[u];
-      const int nk = len < max_depth ? sh.off[u + 1] - o : 0;
-      if (nk > 1) {
-        err = true;
-        break;
-      }
-      const uint64_t Zu = sh.u.s.rz[u];
-      if (nk == 0) {
-        // end of the chain: the emitted token comes from the target row
-        bonus = final_draw(u, Zu, 0, czu);
-        break;
-      }
-      list_children(u, 1);
-      const int c = sh.kids[0];
-      const double qt = sh.v.qt[c];
-      if (qt != qt) {  // depth outside [1, K]
-        err = true;
-        break;
-      }
-      const int t = sh.tkn[c];
-      const double pt = (t >= 0 && t < V) ? (double)sh.u.s.wc[c] / (double)Zu : 0.0;
-      const uint64_t d = sh.u.s.draw[o];
-      const double u53 = (double)(d >> 11) * 0x1p-53;
-      // min(1, p/q): a token the target gives no mass is never accepted
-      if (pt > 0.0 && (pt >= qt || u53 < pt / qt)) {
-        ++len;
-        if (lane == 0) {
-          acc_nodes[len] = c;
-          out_tok[len - 1] = t;
-        }
-        u = c;
-        continue;
-      }
-      // rejection: the residual (p - q)+ is drawn by the kernels that follow
+      wave_lds_sync();
+      const uint64_t Zres = sh.r.rz[u] - wave_sum_u64(zx);
+      const uint64_t cw = lane < C ? czu - sh.czsub[lane] : 0ull;
+      const uint64_t R = scaled_draw(d0, d1, Zres);
+      const uint64_t incl = wave_incl_scan_u64(cw);
+      const uint64_t hit = __ballot(lane < C && incl > R);
+      const int cs = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
+      const uint64_t before = cs >= 0 ? readlane_u64(incl - cw, cs) : 0ull;
       if (lane == 0) {
-        const int dd = depth[rb + c];
-        DraftPending pd;
-        pd.flag = 1;
-        pd.u = u;
-        pd.dd = dd;
-        pd.len = len;
-        pd.mu = sh.rmax[u];
-        pd.mq = sh.dmax[dd - 1];
-        pd.zu = Zu;
-        pd.zq = sh.dz[dd - 1];
-        if (u < nres) {
-          pd.d0 = sh.rd0[u];
-          pd.d1 = sh.rd1[u];
-        } else {
-          const u64x4 dr = philox4x64_10(round, (uint64_t)b, (uint64_t)u, kResidualSlot, seed, 0);
-          pd.d0 = dr.v[0];
-          pd.d1 = dr.v[1];
-        }
-        pend[b] = pd;
+        sh.cs = cs;
+        sh.r2 = R - before;
       }
-      pending = true;
-      break;
+    }
+    __syncthreads();
+    const int cs = sh.cs;
+    if (cs >= 0) {
+      const int base = cs * kAcceptChunk;
+      float x[16];
+      ChunkLoad<T>::load(target + grow * (int64_t)V, base, V, x);
+      const float m = sh.rmax[u];
+      uint64_t w[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) w[j] = weight(x[j], m, inv_t);
+      // excluded tokens among this thread's 16, as a bit mask
+      const int lo = base + 16 * tid;
+      uint32_t xm = 0;
+      for (int e0 = 0; e0 < nk; e0 += 8) {
+        int te[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) te[q] = sh.par[min(e0 + q, nk - 1)];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t rel = (uint32_t)(te[q] - lo);
+          xm |= rel < 16u ? 1u << rel : 0u;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if ((xm >> j) & 1u) w[j] = 0;
+      const int tok = block_pick(w, base, sh.r2, sh.pz, sh.wfirst, &sh.tok);
+      bonus = tok == 0x7fffffff ? -1 : tok;
     }
   }
-  if (lane == 0) {
+  if (tid == 0) {
     if (err) {
       accept_len[b] = -1;
     } else if (!pending) {
@@ -796,44 +799,6 @@ __global__ __launch_bounds__(kAccNT) void k_draft_resid(const T* __restrict__ ta
   if (threadIdx.x == 0) rcz[(int64_t)b * kMaxChunks + c] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
 }
 
-// Smallest token of chunk `base` whose running sum exceeds R, given the 16
-// consecutive weights of each thread (thread t: tokens base + 16t ...).
-__device__ int block_pick(const uint64_t (&w)[16], int base, uint64_t R, uint64_t* tsum,
-                          int* tok) {
-  const int tid = threadIdx.x;
-  uint64_t run = 0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) run += w[j];
-  tsum[tid] = run;
-  if (tid == 0) *tok = 0x7fffffff;
-  __syncthreads();
-  if (tid < WAVE) {
-    const uint64_t a0 = tsum[4 * tid], a1 = tsum[4 * tid + 1], a2 = tsum[4 * tid + 2],
-                   a3 = tsum[4 * tid + 3];
-    const uint64_t s4 = a0 + a1 + a2 + a3;
-    uint64_t ex = wave_incl_scan_u64(s4) - s4;
-    tsum[4 * tid] = ex;
-    ex += a0;
-    tsum[4 * tid + 1] = ex;
-    ex += a1;
-    tsum[4 * tid + 2] = ex;
-    ex += a2;
-    tsum[4 * tid + 3] = ex;
-  }
-  __syncthreads();
-  uint64_t acc = tsum[tid];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    acc += w[j];
-    if (acc > R) {
-      atomicMin(tok, base + 16 * tid + j);
-      break;
-    }
-  }
-  __syncthreads();
-  return *tok;
-}
-
 // the residual draw of each pending sequence (the target row itself if the
 // residual is empty to rounding)
 template <typename T>
@@ -844,6 +809,7 @@ __global__ __launch_bounds__(kAccNT) void k_draft_pick(
     int* __restrict__ accept_len, int* __restrict__ out_tokens) {
   __shared__ uint64_t tsum[kAccNT];
   __shared__ int s_cs, s_tok;
+  __shared__ int s_wfirst[kAccNT / WAVE];
   __shared__ uint64_t s_r;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id();
@@ -883,7 +849,7 @@ __global__ __launch_bounds__(kAccNT) void k_draft_pick(
 #pragma unroll
       for (int j = 0; j < 16; ++j) w[j] = weight(x[j], pd.mu, inv_t);
     }
-    tok = block_pick(w, base, s_r, tsum, &s_tok);
+    tok = block_pick(w, base, s_r, tsum, s_wfirst, &s_tok);
     if (tok == 0x7fffffff) tok = -1;
   }
   if (tid == 0) {
@@ -911,7 +877,8 @@ AcceptPlan accept_plan(int batch, int N, int K, int V, bool sampled, bool draft)
   p.off_cmax = take((size_t)p.rows * p.C * sizeof(float));
   p.off_carg = take((size_t)p.rows * p.C * sizeof(int));
   p.off_cz = sampled ? take((size_t)p.rows * p.C * sizeof(uint64_t)) : 0;
-  p.off_cseg = sampled ? take((size_t)p.rows * p.C * kSegs * sizeof(uint64_t)) : 0;
+  p.off_wtg = sampled ? take((size_t)batch * N * sizeof(uint64_t)) : 0;
+  p.off_wqg = draft ? take((size_t)batch * N * sizeof(uint64_t)) : 0;
   p.off_rcz = draft ? take((size_t)batch * kMaxChunks * sizeof(uint64_t)) : 0;
   p.off_pend = draft ? take((size_t)batch * sizeof(DraftPending)) : 0;
   p.workspace = off;
@@ -928,7 +895,8 @@ static void launch_accept_t(const AcceptPlan& p, const T* target, const T* draft
   float* cmax = reinterpret_cast<float*>(w + p.off_cmax);
   int* carg = reinterpret_cast<int*>(w + p.off_carg);
   uint64_t* cz = sampled ? reinterpret_cast<uint64_t*>(w + p.off_cz) : nullptr;
-  uint64_t* cseg = sampled ? reinterpret_cast<uint64_t*>(w + p.off_cseg) : nullptr;
+  uint64_t* wtg = sampled ? reinterpret_cast<uint64_t*>(w + p.off_wtg) : nullptr;
+  uint64_t* wqg = draft_proposal ? reinterpret_cast<uint64_t*>(w + p.off_wqg) : nullptr;
   uint64_t* rcz = draft_proposal ? reinterpret_cast<uint64_t*>(w + p.off_rcz) : nullptr;
   DraftPending* pend =
       draft_proposal ? reinterpret_cast<DraftPending*>(w + p.off_pend) : nullptr;
@@ -939,7 +907,7 @@ static void launch_accept_t(const AcceptPlan& p, const T* target, const T* draft
     hipLaunchKernelGGL((k_rowmax<T, false>), g, blk, 0, stream, target, draft, V, trows,
                        p.rows, cmax, carg);
     hipLaunchKernelGGL((k_rowz<T>), g, blk, 0, stream, target, draft, V, p.C, trows, p.rows,
-                       inv_t, cmax, cz, cseg);
+                       inv_t, cmax, cz, N, K, parent, token, depth, n_nodes, wtg, wqg);
   } else {
     hipLaunchKernelGGL((k_rowmax<T, true>), g, blk, 0, stream, target, draft, V, trows, p.rows,
                        cmax, carg);
@@ -947,7 +915,7 @@ static void launch_accept_t(const AcceptPlan& p, const T* target, const T* draft
 #define TV_WALK(M)                                                                            \
   hipLaunchKernelGGL((k_walk<T, M>), dim3(batch), blk, 0, stream, target, draft, N, K, V, p.C, \
                      parent, token, depth, n_nodes, inv_t, seed, round, max_depth, cmax, carg, \
-                     cz, cseg, trows, p.rows, accept_len, accepted_nodes, out_tokens, pend)
+                     cz, wtg, wqg, trows, p.rows, accept_len, accepted_nodes, out_tokens, pend)
   if (!sampled) {
     TV_WALK(kGreedy);
   } else if (!draft_proposal) {

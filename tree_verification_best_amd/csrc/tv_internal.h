@@ -62,9 +62,10 @@ struct AcceptPlan {
   int chunk, C;
   int64_t rows;  // batch * N target rows (+ batch * K draft rows in DRAFT mode)
   bool draft_rows;
-  // chunk records, chunk-major ([C][rows]); segment sums [rows][C][16]; DRAFT
+  // chunk records, chunk-major ([C][rows]); the weight of each child's token
+  // in its parent's row (and, DRAFT, in its drafter row) [batch][N]; DRAFT
   // residual chunk sums [batch][64] and the per-sequence hand-over record
-  size_t off_cmax, off_carg, off_cz, off_cseg, off_rcz, off_pend;
+  size_t off_cmax, off_carg, off_cz, off_wtg, off_wqg, off_rcz, off_pend;
   size_t workspace;
 };
 
