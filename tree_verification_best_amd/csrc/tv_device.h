@@ -302,6 +302,44 @@ __device__ __forceinline__ void wave_argmax(float& v, int& id) {
 }
 
 // ---------------------------------------------------------------------------
+// Order keys: (value, id) pairs in the order above as one unsigned 64-bit
+// integer, larger = better: the float's bits made monotone (negative values
+// bit-inverted, the sign bit set on the others; -0 is taken as +0, which
+// compares equal to it), then the inverted id.  Logits are never NaN.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t order_key(float v, int id) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v + 0.0f);  // -0 -> +0
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t k = (uint32_t)(key >> 32);
+  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+__device__ __forceinline__ int key_id(uint64_t key) {
+  return (int)(0xFFFFFFFFu - (uint32_t)key);
+}
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+// one step of a wave-wide u64 minimum (lanes without a source read ~0)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_min_u64_step(uint64_t v) {
+  const uint32_t lo = dpp_or<CTRL, ROWS>(0xFFFFFFFFu, (uint32_t)v);
+  const uint32_t hi = dpp_or<CTRL, ROWS>(0xFFFFFFFFu, (uint32_t)(v >> 32));
+  return umin64(v, ((uint64_t)hi << 32) | lo);
+}
+// minimum over the wave (every lane gets it)
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+  v = dpp_min_u64_step<0x111, 0xF>(v);
+  v = dpp_min_u64_step<0x112, 0xF>(v);
+  v = dpp_min_u64_step<0x114, 0xF>(v);
+  v = dpp_min_u64_step<0x118, 0xF>(v);
+  v = dpp_min_u64_step<0x142, 0xA>(v);
+  v = dpp_min_u64_step<0x143, 0xC>(v);
+  return readlane_u64(v, WAVE - 1);
+}
+
+// ---------------------------------------------------------------------------
 // Block-wide top-k (k <= 64) of E (value, id) items per thread, in the order
 // above.  Result: out_v / out_i [k] in LDS-or-global memory, best first.
 // Items with id >= first_pad are padding: they never enter the result; if
@@ -311,16 +349,18 @@ __device__ __forceinline__ void wave_argmax(float& v, int& id) {
 // Each wave takes the k-th best of its 64 per-thread maxima as a threshold
 // (every item of the wave's top-k is at least as good, so the survivors
 // contain the block's top-k), keeps the items at least as good as its
-// threshold, and the survivors are ranked by counting.  If a wave keeps more
-// than kCap items (heavy ties) the block falls back to k rounds of argmax.
-// Requires blockDim.x == NT, a multiple of 64, and the scratch below.
+// threshold, and the survivors are ranked by counting.  All comparisons are
+// on order keys; the counting reads LDS in batches of eight.  If a wave
+// keeps more than kCap items (heavy ties) the block falls back to k rounds
+// of argmax.  Requires blockDim.x == NT, a multiple of 64, and the scratch
+// below.
 // ---------------------------------------------------------------------------
 template <int NT>
 struct TopkScratch {
   static constexpr int kWaves = NT / WAVE;
   static constexpr int kCap = 256;
-  float sv[kWaves * kCap];
-  int si[kWaves * kCap];
+  uint64_t sk[kWaves * kCap];  // survivors' keys, per-wave segments
+  uint64_t lk[NT];             // per-thread best keys
   int wcount[kWaves];
   int overflow;
   float rv[kWaves];
@@ -333,67 +373,79 @@ __device__ void block_topk(float (&val)[E], int (&id)[E], int k, TopkScratch<NT>
                            int pad_base = 0x7fffffff) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
   constexpr int kCap = TopkScratch<NT>::kCap;
+  constexpr int kW = NT / WAVE;
   if (tid == 0) sc.overflow = 0;
-  // per-thread best
-  float bv = val[0];
-  int bi = id[0];
+  // keys (padding: 0, below every real key) and the per-thread best
+  uint64_t key[E];
+  uint64_t best = 0;
 #pragma unroll
-  for (int e = 1; e < E; ++e)
-    if (vi_better(val[e], id[e], bv, bi)) {
-      bv = val[e];
-      bi = id[e];
-    }
-  // rank of this lane's best among the wave's 64 (all pairs are distinct)
-  int rank = 0;
-  for (int j = 0; j < WAVE; ++j) {
-    float ov = readlane_f(bv, j);
-    int oi = readlane_i(bi, j);
-    rank += vi_better(ov, oi, bv, bi) ? 1 : 0;
+  for (int e = 0; e < E; ++e) {
+    key[e] = id[e] < first_pad ? order_key(val[e], id[e]) : 0ull;
+    best = best > key[e] ? best : key[e];
   }
-  uint64_t hit = __ballot(rank == k - 1);
-  int tl = __ffsll((unsigned long long)hit) - 1;
-  float tv = readlane_f(bv, tl);
-  int ti = readlane_i(bi, tl);
-  // survivors: items at least as good as the threshold
+  // wave threshold: the k-th largest of the 64 lane bests (0 if fewer than
+  // k are real), i.e. the smallest best whose rank is below k
+  sc.lk[tid] = best;
+  __syncthreads();  // also publishes the overflow flag
+  const uint64_t* wk = sc.lk + wave * WAVE;
+  int rank = 0;
+#pragma unroll
+  for (int j0 = 0; j0 < WAVE; j0 += 16) {
+    uint64_t o[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) o[q] = wk[j0 + q];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) rank += o[q] > best ? 1 : 0;
+  }
+  const uint64_t thr = wave_min_u64(rank < k ? best : ~0ull);
+  // survivors: real items at least as good as the threshold
   int cnt = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) cnt += (id[e] < first_pad && !vi_better(tv, ti, val[e], id[e])) ? 1 : 0;
-  int incl = wave_incl_scan_i(cnt);
-  int total = readlane_i(incl, WAVE - 1);
-  __syncthreads();  // overflow flag initialised
+  for (int e = 0; e < E; ++e) cnt += (key[e] != 0 && key[e] >= thr) ? 1 : 0;
+  const int incl = wave_incl_scan_i(cnt);
+  const int total = readlane_i(incl, WAVE - 1);
   if (total > kCap) {
     if (lane == 0) sc.overflow = 1;
   } else {
-    int off = incl - cnt;
+    int off = wave * kCap + incl - cnt;
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (id[e] < first_pad && !vi_better(tv, ti, val[e], id[e])) {
-        sc.sv[wave * kCap + off] = val[e];
-        sc.si[wave * kCap + off] = id[e];
-        ++off;
-      }
+      if (key[e] != 0 && key[e] >= thr) sc.sk[off++] = key[e];
   }
   if (lane == 0) sc.wcount[wave] = total;
   __syncthreads();
   if (!sc.overflow) {
-    // rank survivors by counting; survivors live in per-wave segments
-    int nsurv = 0;
-    for (int w = 0; w < NT / WAVE; ++w) nsurv += sc.wcount[w];
+    // rank survivors by counting the better ones
+    int wc[kW], nsurv = 0;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+      wc[w] = sc.wcount[w];
+      nsurv += wc[w];
+    }
     for (int t = tid; t < nsurv; t += NT) {
       int w = 0, loc = t;
-      while (loc >= sc.wcount[w]) {
-        loc -= sc.wcount[w];
-        ++w;
-      }
-      float xv = sc.sv[w * kCap + loc];
-      int xi = sc.si[w * kCap + loc];
+#pragma unroll
+      for (int w2 = 0; w2 < kW - 1; ++w2)
+        if (w == w2 && loc >= wc[w2]) {
+          loc -= wc[w2];
+          w = w2 + 1;
+        }
+      const uint64_t x = sc.sk[w * kCap + loc];
       int r = 0;
-      for (int w2 = 0; w2 < NT / WAVE; ++w2)
-        for (int j = 0; j < sc.wcount[w2]; ++j)
-          r += vi_better(sc.sv[w2 * kCap + j], sc.si[w2 * kCap + j], xv, xi) ? 1 : 0;
+#pragma unroll
+      for (int w2 = 0; w2 < kW; ++w2) {
+        const uint64_t* seg = sc.sk + w2 * kCap;
+        for (int j0 = 0; j0 < wc[w2]; j0 += 8) {
+          uint64_t o[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) o[q] = seg[min(j0 + q, wc[w2] - 1)];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) r += (j0 + q < wc[w2] && o[q] > x) ? 1 : 0;
+        }
+      }
       if (r < k) {
-        out_v[r] = xv;
-        out_i[r] = xi;
+        out_v[r] = key_value(x);
+        out_i[r] = key_id(x);
       }
     }
     for (int r = nsurv + tid; r < k; r += NT) {
