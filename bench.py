@@ -2,6 +2,8 @@
 
 A step is the whole round on one batch of synthetic input already resident in
 HBM: tv_tree_build -> tv_tree_attention_verify (one layer) -> tv_tree_accept.
+The KV commit that closes a round (tv_kv_commit) is timed after the steps, in
+a loop of its own, and reported as per_call.commit.
 The default workload is the 4B-class GQA layer (32 query / 8 KV heads, head
 dim 128, bf16, context 4096, K = 16 draft positions, top-8, budget 64,
 vocabulary 151936, sampled acceptance at T = 1).  Inputs rotate over enough
@@ -225,6 +227,7 @@ def main():
     lse = torch.empty((b, N, c["Hq"]), dtype=torch.float32, device=dev)
     acc = dict(accept_len=torch.empty((b,), **i32), accepted_nodes=torch.empty((b, K + 1), **i32),
                out_tokens=torch.empty((b, K + 1), **i32))
+    new_ctx = torch.empty((b,), **i32)
     if not c["build"]:
         tree["parent"].copy_(tree_in[0])
         tree["token"].copy_(tree_in[1])
@@ -252,6 +255,13 @@ def main():
                           max_depth=K, workspace=ws_c, out=acc)
         if ev is not None:
             ev[3].record(stream)
+
+    def commit_(step):
+        # the accepted path's K/V rows move behind the context (in place; the
+        # input set's context lengths are kept, so every call sees the same shapes)
+        s = sets[step % nsets]
+        tv.tv_kv_commit(s["k"], s["v"], s["ctx"], acc["accept_len"], acc["accepted_nodes"],
+                        new_ctx_len=new_ctx)
 
     graphs = None
     if args.graph:
@@ -301,12 +311,26 @@ def main():
     if graphs is None:
         for name, (a, z) in (("build", (0, 1)), ("attention", (1, 2)), ("accept", (2, 3))):
             calls[name] = sum(evs[i][a].elapsed_time(evs[i][z]) for i in range(args.steps)) / args.steps
+    # the commit, outside the timed steps (acc holds the last step's walk)
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        cev[i][0].record(stream)
+        commit_(i)
+        cev[i][1].record(stream)
+    torch.cuda.synchronize()
+    calls["commit"] = sum(a.elapsed_time(z) for a, z in cev) / args.steps
 
     # ---- accounting ------------------------------------------------------
     nn_h = tree["n_nodes"].cpu().numpy()
     dep_h = tree["depth"].cpu().numpy()
     Lsum = int(ctx0.sum())
     abytes = algorithmic_bytes(c, b, N, Lsum, c["build"])
+    # the commit reads and writes each accepted draft's K and V rows once
+    # (the last step's accept lengths stand for the mean)
+    el = 2 if c["dtype"] == "bf16" else 4
+    moved = float(acc["accept_len"].clamp(min=0).sum().item())
+    abytes["commit"] = int(2 * 2 * c["Hkv"] * c["D"] * el * moved)
     aflops = attention_flops(c, nn_h, dep_h, ctx0)
     rows = b * N * c["Hq"]
     rounds_per_s = 1e3 / ms_per_step

@@ -232,6 +232,33 @@ tv_status tv_tree_accept(const void *target_logits, const void *draft_logits, tv
                          int32_t *accepted_nodes, int32_t *out_tokens, void *workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * tv_kv_commit -- keep the accepted path in the target KV cache.
+ *
+ * Primer, "KV cache handling": after verification only the accepted tokens
+ * stay in the target cache; the entries of the rejected candidates are
+ * dropped (rolled back).  After a round, cache row L_b + i holds tree node i
+ * (as tv_tree_attention_verify reads it); the committed sequence is the root
+ * followed by the accepted drafts, accepted_nodes[b][0..accept_len[b]] as
+ * written by tv_tree_accept.  This call moves row L_b + accepted_nodes[b][j]
+ * to row L_b + j for j = 0..accept_len[b], in both caches and every KV head,
+ * in place, and sets new_ctx_len[b] = L_b + accept_len[b] + 1.  Rows past the
+ * new length are left as they are, free for the next round.
+ *   k_cache, v_cache [batch][Hkv][cap][D]  dtype dt, modified in place
+ *   ctx_len, accept_len     int32 [batch]
+ *   accepted_nodes          int32 [batch][width]
+ *   new_ctx_len             int32 [batch], may be the ctx_len array itself
+ * Per sequence: accept_len < 0 (a refused tree) commits nothing and gives
+ * new_ctx_len = L_b; a path that does not start at node 0, does not increase
+ * strictly, or reaches row cap or beyond is left uncommitted with
+ * new_ctx_len = -1.
+ * Limits: D in {64, 128}; width <= 1024.
+ * ------------------------------------------------------------------------ */
+tv_status tv_kv_commit(void *k_cache, void *v_cache, tv_dtype dt, int batch, int Hkv, int cap,
+                       int D, const int32_t *ctx_len, const int32_t *accept_len,
+                       const int32_t *accepted_nodes, int width, int32_t *new_ctx_len,
+                       hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

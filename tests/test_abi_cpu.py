@@ -20,7 +20,7 @@ def _declared():
 
 def test_header_functions_exported():
     names = _declared()
-    assert len(names) == 9
+    assert len(names) == 10
     lib = ctypes.CDLL(tv.LIBPATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -158,3 +158,24 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         tv.tv_tree_build(x, 4, 8, torch.zeros(1, dtype=torch.int32),
                          torch.zeros(1, dtype=torch.int32))
+
+
+def _commit(**kw):
+    a = dict(k=FAKE, v=FAKE, dt=1, batch=1, Hkv=2, cap=64, D=128, ctx=FAKE, al=FAKE, an=FAKE,
+             width=17, new=FAKE)
+    a.update(kw)
+    return tv.lib().tv_kv_commit(a["k"], a["v"], a["dt"], a["batch"], a["Hkv"], a["cap"],
+                                 a["D"], a["ctx"], a["al"], a["an"], a["width"], a["new"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), tv.TV_ERR_INVALID),
+    (dict(new=None), tv.TV_ERR_INVALID),
+    (dict(dt=4), tv.TV_ERR_INVALID),
+    (dict(batch=0), tv.TV_ERR_INVALID),
+    (dict(width=0), tv.TV_ERR_INVALID),
+    (dict(D=96), tv.TV_ERR_UNSUPPORTED),
+    (dict(width=1025), tv.TV_ERR_UNSUPPORTED),
+])
+def test_commit_rejects(kw, status):
+    assert _commit(**kw) == status

@@ -12,6 +12,7 @@ raise.
     tv_tree_ancestors        depth / positions / ancestor rows of a parent array
     tv_tree_attention_verify tree-masked GQA attention over context + tree
     tv_tree_accept           greedy or sampled acceptance walk
+    tv_kv_commit             keep the accepted path in the KV cache
 """
 import ctypes
 import math
@@ -29,7 +30,7 @@ TV_PROPOSAL_POINT_MASS, TV_PROPOSAL_DRAFT = 0, 1
 
 EXPORTS = ("tv_status_string", "tv_version", "tv_tree_build_workspace", "tv_tree_build",
            "tv_tree_ancestors", "tv_tree_attention_workspace", "tv_tree_attention_verify",
-           "tv_tree_accept_workspace", "tv_tree_accept")
+           "tv_tree_accept_workspace", "tv_tree_accept", "tv_kv_commit")
 
 _lib = None
 
@@ -72,6 +73,8 @@ def _load():
     L.tv_tree_accept.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, f32, i32,
                                  u64, u64, i32, vp, vp, vp, vp, sz, vp]
     L.tv_tree_accept.restype = i32
+    L.tv_kv_commit.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
+    L.tv_kv_commit.restype = i32
     _lib = L
     return L
 
@@ -240,3 +243,20 @@ def tv_tree_accept(target_logits, parent, token, depth, n_nodes, *, mode, max_de
                           _stream(dev))
     _check(st, "tv_tree_accept")
     return out
+
+
+def tv_kv_commit(k_cache, v_cache, ctx_len, accept_len, accepted_nodes, new_ctx_len=None):
+    """Moves the accepted path's K/V rows behind the context, in place; returns
+    new_ctx_len [b] (a new tensor unless one is given; ctx_len itself may be)."""
+    L = _load()
+    b, Hkv, cap, D = k_cache.shape
+    if new_ctx_len is None:
+        new_ctx_len = torch.empty((b,), dtype=torch.int32, device=k_cache.device)
+    st = L.tv_kv_commit(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache", k_cache.dtype),
+                        _dt(k_cache), b, Hkv, cap, D, _dev(ctx_len, "ctx_len", torch.int32),
+                        _dev(accept_len, "accept_len", torch.int32),
+                        _dev(accepted_nodes, "accepted_nodes", torch.int32),
+                        accepted_nodes.shape[1], _dev(new_ctx_len, "new_ctx_len", torch.int32),
+                        _stream(k_cache.device))
+    _check(st, "tv_kv_commit")
+    return new_ctx_len

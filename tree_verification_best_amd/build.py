@@ -28,6 +28,7 @@ SOURCES = {
     "tv_build.hip": ["-ffp-contract=off"],
     "tv_accept.hip": ["-ffp-contract=off"],
     "tv_attention.hip": ["-fno-honor-nans"],
+    "tv_commit.hip": [],
     "tv_api.cpp": ["-ffp-contract=off", "-x", "hip"],
 }
 

@@ -168,4 +168,20 @@ tv_status tv_tree_accept(const void* target_logits, const void* draft_logits, tv
                                           workspace, stream));
 }
 
+// ---------------------------------------------------------------------------
+tv_status tv_kv_commit(void* k_cache, void* v_cache, tv_dtype dt, int batch, int Hkv, int cap,
+                       int D, const int32_t* ctx_len, const int32_t* accept_len,
+                       const int32_t* accepted_nodes, int width, int32_t* new_ctx_len,
+                       hipStream_t stream) {
+  if (!k_cache || !v_cache || !ctx_len || !accept_len || !accepted_nodes || !new_ctx_len)
+    return TV_ERR_INVALID;
+  if (dt != TV_F32 && dt != TV_BF16) return TV_ERR_INVALID;
+  if (batch < 1 || Hkv < 1 || cap < 1 || width < 1) return TV_ERR_INVALID;
+  if ((D != 64 && D != 128) || width > tvk::kCommitMaxWidth || batch > 0x7fffffff)
+    return TV_ERR_UNSUPPORTED;
+  return device_status(tvk::launch_kv_commit(k_cache, v_cache, dt == TV_BF16 ? 2 : 4, batch, Hkv,
+                                             cap, D, ctx_len, accept_len, accepted_nodes, width,
+                                             new_ctx_len, stream));
+}
+
 }  // extern "C"

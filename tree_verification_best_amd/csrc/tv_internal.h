@@ -77,4 +77,11 @@ hipError_t launch_accept(const AcceptPlan& p, const void* target, const void* dr
                          int max_depth, int* accept_len, int* accepted_nodes, int* out_tokens,
                          void* ws, hipStream_t stream);
 
+// ---- KV commit ----
+constexpr int kCommitMaxWidth = 1024;
+hipError_t launch_kv_commit(void* k_cache, void* v_cache, int elem_bytes, int batch, int Hkv,
+                            int cap, int D, const int* ctx_len, const int* accept_len,
+                            const int* accepted_nodes, int width, int* new_ctx_len,
+                            hipStream_t stream);
+
 }  // namespace tvk
