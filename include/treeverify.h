@@ -166,7 +166,8 @@ tv_status tv_tree_ancestors(const int32_t *parent, const int32_t *n_nodes,
  *         one head's cache rows (cap * D * 2 bytes) below 2 GiB (TV_ERR_UNSUPPORTED).
  * bf16: bf16 products on the matrix cores with fp32 accumulation and an
  * fp32 online softmax; the softmax weights enter the second product
- * rounded to bf16 while the normaliser sums them in fp32.  f32: fp32
+ * rounded to bf16 while the normaliser sums them in fp32; each context
+ * split's normalised partial result is kept in fp16 (|V| < 65504).  f32: fp32
  * throughout (vector ALU).
  * ------------------------------------------------------------------------ */
 size_t tv_tree_attention_workspace(int batch, int N, int Hq, int Hkv, int D, int max_ctx,

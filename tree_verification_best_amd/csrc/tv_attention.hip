@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int* __restrict__ ctx_len,
     const uint64_t* __restrict__ anc, const int* __restrict__ n_nodes, int N, int Hq, int Hkv,
-    int cap, int S, int KS, int MT, int items, float scale_log2, float* __restrict__ Opart,
+    int cap, int S, int KS, int MT, int items, float scale_log2, uint16_t* __restrict__ Opart,
     float* __restrict__ Mpart, float* __restrict__ Lpart, int batch) {
   constexpr int KP = D + 8;   // K tile pitch (bf16): 16-byte reads spread over banks
   constexpr int VP = D + 16;  // V tile pitch (bf16): the 16 rows of a transposing read
@@ -324,25 +324,34 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
       Mpart[pr] = m_run * scale_log2;  // log2 domain (-inf stays -inf)
       Lpart[pr] = l_tot;
     }
-    float* op = Opart + pr * D;
+    // O / l in fp16: a weighted mean of V rows, so it stays within V's range
+    const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* op = Opart + pr * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d0 = 32 * db + 8 * j + 4 * half;
-        *reinterpret_cast<float4*>(op + d0) =
-            make_float4(oacc[db][4 * j], oacc[db][4 * j + 1], oacc[db][4 * j + 2],
-                        oacc[db][4 * j + 3]);
+        uint32_t w2[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const _Float16 x0 = (_Float16)(oacc[db][4 * j + 2 * t] * inv_l);
+          const _Float16 x1 = (_Float16)(oacc[db][4 * j + 2 * t + 1] * inv_l);
+          w2[t] = (uint32_t)__builtin_bit_cast(uint16_t, x0) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
+        }
+        *reinterpret_cast<uint2*>(op + d0) = make_uint2(w2[0], w2[1]);
       }
   }
 }
 
-// Merge the S + 1 partials of every query row: weights 2^(m_s - M) / L with
-// L = sum_s 2^(m_s - M) l_s.  One thread per (row, head, 4 output columns):
+// Merge the S + 1 partials of every query row.  Partial s holds O_s / l_s in
+// fp16; its weight is 2^(m_s - M) l_s / L with L = sum_s 2^(m_s - M) l_s.
+// One thread per (row, head, 4 output columns):
 // the D/4 threads of a row read the same (m_s, l_s) words, and every load of
 // a batch of splits is issued before the first is used.
 template <typename OutT>
-__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ Opart,
+__global__ __launch_bounds__(256) void k_attn_combine(const uint16_t* __restrict__ Opart,
                                                      const float* __restrict__ Mpart,
                                                      const float* __restrict__ Lpart,
                                                      const int* __restrict__ n_nodes, int batch,
@@ -385,17 +394,22 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
       const int s = min(s0 + j, S1 - 1);
       ms[j] = Mpart[s * plane + r];
       ls[j] = Lpart[s * plane + r];
-      o[j] = *reinterpret_cast<const float4*>(Opart + (s * plane + r) * D + 4 * d4);
+      const uint2 h = *reinterpret_cast<const uint2*>(Opart + (s * plane + r) * D + 4 * d4);
+      o[j] = make_float4((float)__builtin_bit_cast(_Float16, (uint16_t)(h.x & 0xFFFFu)),
+                         (float)__builtin_bit_cast(_Float16, (uint16_t)(h.x >> 16)),
+                         (float)__builtin_bit_cast(_Float16, (uint16_t)(h.y & 0xFFFFu)),
+                         (float)__builtin_bit_cast(_Float16, (uint16_t)(h.y >> 16)));
     }
 #pragma unroll
     for (int j = 0; j < kB; ++j) {
       const bool live = s0 + j < S1 && ms[j] != -__builtin_inff();
       const float wgt = live ? __builtin_amdgcn_exp2f(ms[j] - M) : 0.f;
-      lsum += wgt * ls[j];
-      acc.x += wgt * o[j].x;
-      acc.y += wgt * o[j].y;
-      acc.z += wgt * o[j].z;
-      acc.w += wgt * o[j].w;
+      const float wl = wgt * ls[j];  // the partial holds O / l
+      lsum += wl;
+      acc.x += wl * o[j].x;
+      acc.y += wl * o[j].y;
+      acc.z += wl * o[j].z;
+      acc.w += wl * o[j].w;
     }
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
@@ -515,7 +529,7 @@ AttnPlan attention_plan(int batch, int N, int Hq, int Hkv, int D, int max_ctx, i
     off += (bytes + 255) & ~(size_t)255;
     return o;
   };
-  p.off_o = take(rows * D * sizeof(float));
+  p.off_o = take(rows * D * sizeof(uint16_t));  // fp16 O / l
   p.off_ml = take(rows * 2 * sizeof(float));
   p.workspace = off;
   return p;
@@ -536,7 +550,7 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, con
     return hipGetLastError();
   }
   char* w = static_cast<char*>(ws);
-  float* Opart = reinterpret_cast<float*>(w + p.off_o);
+  uint16_t* Opart = reinterpret_cast<uint16_t*>(w + p.off_o);
   const size_t prow = (size_t)(p.splits + 1) * rows;
   float* Mpart = reinterpret_cast<float*>(w + p.off_ml);
   float* Lpart = Mpart + prow;
