@@ -615,9 +615,20 @@ hipError_t launch_build(const BuildPlan& p, const void* draft, bool bf16, int ba
   }
   hipLaunchKernelGGL((k_finalize<kFinalizeE>), dim3((unsigned)p.rows), dim3(kBuildNT), 0,
                      stream, V, p.C, p.chunk, topk, inv_t, cval, cid, cz, ftok, fq);
-  hipLaunchKernelGGL((k_select<kBuildNT>), dim3(batch), dim3(kBuildNT), p.select_lds, stream,
-                     ftok, fq, K, topk, budget, p.P, root_token, ctx_len, parent, token, depth,
-                     pos, score, anc, n_nodes);
+  // one workgroup per sequence; larger budgets have longer candidate lists,
+  // whose counting passes gain from more waves (measured: 256 threads up to
+  // budget 127, 512 up to 511, then 1024)
+#define TV_SELECT(NT)                                                                        \
+  hipLaunchKernelGGL((k_select<NT>), dim3(batch), dim3(NT), p.select_lds, stream, ftok, fq, K, \
+                     topk, budget, p.P, root_token, ctx_len, parent, token, depth, pos, score,  \
+                     anc, n_nodes)
+  if (budget < 128)
+    TV_SELECT(256);
+  else if (budget < 512)
+    TV_SELECT(512);
+  else
+    TV_SELECT(1024);
+#undef TV_SELECT
   return hipGetLastError();
 }
 
