@@ -2,8 +2,9 @@
 
 A step is the whole round on one batch of synthetic input already resident in
 HBM: tv_tree_build -> tv_tree_attention_verify (one layer) -> tv_tree_accept.
-The KV commit that closes a round (tv_kv_commit) is timed after the steps, in
-a loop of its own, and reported as per_call.commit.
+The KV commit that closes a round (tv_kv_commit) and the cost-aware tree size
+(tv_tree_budget) are timed after the steps, as replays of captured graphs, and
+reported as per_call.commit and per_call.budget.
 The default workload is the 4B-class GQA layer (32 query / 8 KV heads, head
 dim 128, bf16, context 4096, K = 16 draft positions, top-8, budget 64,
 vocabulary 151936, sampled acceptance at T = 1).  Inputs rotate over enough
@@ -311,16 +312,42 @@ def main():
     if graphs is None:
         for name, (a, z) in (("build", (0, 1)), ("attention", (1, 2)), ("accept", (2, 3))):
             calls[name] = sum(evs[i][a].elapsed_time(evs[i][z]) for i in range(args.steps)) / args.steps
-    # the commit, outside the timed steps (acc holds the last step's walk):
-    # back-to-back calls between two events
+    # the commit, outside the timed steps (acc holds the last step's walk).
+    # One call is shorter than the host's launch path, so the calls are
+    # captured into a graph and the replays timed, as device time.
+    ncommit = 50
+    cg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cg):
+        for i in range(ncommit):
+            commit_(i)
+    cg.replay()
+    torch.cuda.synchronize()
     c0 = torch.cuda.Event(enable_timing=True)
     c1 = torch.cuda.Event(enable_timing=True)
+    reps = 4
     c0.record(stream)
-    for i in range(args.steps):
-        commit_(i)
+    for _ in range(reps):
+        cg.replay()
     c1.record(stream)
     torch.cuda.synchronize()
-    calls["commit"] = c0.elapsed_time(c1) / args.steps
+    calls["commit"] = c0.elapsed_time(c1) / (reps * ncommit)
+    if c["build"]:
+        # the cost-aware tree size over the last step's tree, with an affine
+        # cost per draft node standing in for a measured attention-time sweep
+        cost = torch.tensor([1.0 + 0.01 * i for i in range(N)], dtype=torch.float64, device=dev)
+        n_out = torch.empty((b,), **i32)
+        bg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(bg):
+            for _ in range(ncommit):
+                tv.tv_tree_budget(tree["score"], tree["n_nodes"], cost, n_nodes_out=n_out)
+        bg.replay()
+        torch.cuda.synchronize()
+        c0.record(stream)
+        for _ in range(reps):
+            bg.replay()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        calls["budget"] = c0.elapsed_time(c1) / (reps * ncommit)
 
     # ---- accounting ------------------------------------------------------
     nn_h = tree["n_nodes"].cpu().numpy()
@@ -332,6 +359,7 @@ def main():
     el = 2 if c["dtype"] == "bf16" else 4
     moved = float(acc["accept_len"].clamp(min=0).sum().item())
     abytes["commit"] = int(2 * 2 * c["Hkv"] * c["D"] * el * moved)
+    abytes["budget"] = b * N * 8 + N * 8 + b * 8   # scores and costs in, counts in and out
     aflops = attention_flops(c, nn_h, dep_h, ctx0)
     rows = b * N * c["Hq"]
     rounds_per_s = 1e3 / ms_per_step

@@ -234,6 +234,33 @@ tv_status tv_tree_accept(const void *target_logits, const void *draft_logits, tv
                          size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * tv_tree_budget -- cost-aware size of the tree to verify.
+ *
+ * TAPS sec. 3.2 (key insight) and sec. 4.1 (third stage): verification should
+ * not simply fill the budget; the selector keeps a compact prefix-closed
+ * subtree that maximises the expected accepted tokens per unit of
+ * verification cost.  The rows of a tree from tv_tree_build are in
+ * best-first order, so its first n draft rows are the best prefix-closed
+ * subtree of n nodes, and a round that verifies them emits 1 + S_n tokens in
+ * expectation (S_n = s_1 + ... + s_n, the path scores, as reach
+ * probabilities).  This call keeps
+ *   n* = the smallest n in [0, n_nodes[b] - 1] maximising (1 + S_n) / cost[n]
+ * (S_n summed left to right in fp64, one fp64 division) and sets
+ * n_nodes_out[b] = n* + 1.  Rows past it need no change: attention and the
+ * walk read only rows below n_nodes.
+ *   score    double [batch][N] as written by tv_tree_build (row 0 the root)
+ *   n_nodes  int32 [batch]; a value outside [1, N] is copied unchanged
+ *   cost     double [ncost], ncost >= N: cost[n] > 0 is the measured cost of
+ *            verifying a tree of n draft nodes (e.g. the attention time of
+ *            a round at N = n + 1)
+ *   n_nodes_out int32 [batch], may be the n_nodes array itself
+ * Limits: N <= 1024.
+ * ------------------------------------------------------------------------ */
+tv_status tv_tree_budget(const double *score, const int32_t *n_nodes, const double *cost,
+                         int batch, int N, int ncost, int32_t *n_nodes_out,
+                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * tv_kv_commit -- keep the accepted path in the target KV cache.
  *
  * Primer, "KV cache handling": after verification only the accepted tokens

@@ -20,7 +20,7 @@ def _declared():
 
 def test_header_functions_exported():
     names = _declared()
-    assert len(names) == 10
+    assert len(names) == 11
     lib = ctypes.CDLL(tv.LIBPATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -179,3 +179,11 @@ def _commit(**kw):
 ])
 def test_commit_rejects(kw, status):
     assert _commit(**kw) == status
+
+
+def test_budget_rejects():
+    L = tv.lib()
+    assert L.tv_tree_budget(None, FAKE, FAKE, 1, 8, 8, FAKE, None) == tv.TV_ERR_INVALID
+    assert L.tv_tree_budget(FAKE, FAKE, FAKE, 1, 8, 7, FAKE, None) == tv.TV_ERR_INVALID  # ncost < N
+    assert L.tv_tree_budget(FAKE, FAKE, FAKE, 0, 8, 8, FAKE, None) == tv.TV_ERR_INVALID
+    assert L.tv_tree_budget(FAKE, FAKE, FAKE, 1, 1025, 2000, FAKE, None) == tv.TV_ERR_UNSUPPORTED

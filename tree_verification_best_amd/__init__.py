@@ -12,6 +12,7 @@ raise.
     tv_tree_ancestors        depth / positions / ancestor rows of a parent array
     tv_tree_attention_verify tree-masked GQA attention over context + tree
     tv_tree_accept           greedy or sampled acceptance walk
+    tv_tree_budget           cost-aware tree size (best-first prefix)
     tv_kv_commit             keep the accepted path in the KV cache
 """
 import ctypes
@@ -30,7 +31,7 @@ TV_PROPOSAL_POINT_MASS, TV_PROPOSAL_DRAFT = 0, 1
 
 EXPORTS = ("tv_status_string", "tv_version", "tv_tree_build_workspace", "tv_tree_build",
            "tv_tree_ancestors", "tv_tree_attention_workspace", "tv_tree_attention_verify",
-           "tv_tree_accept_workspace", "tv_tree_accept", "tv_kv_commit")
+           "tv_tree_accept_workspace", "tv_tree_accept", "tv_tree_budget", "tv_kv_commit")
 
 _lib = None
 
@@ -73,6 +74,8 @@ def _load():
     L.tv_tree_accept.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, f32, i32,
                                  u64, u64, i32, vp, vp, vp, vp, sz, vp]
     L.tv_tree_accept.restype = i32
+    L.tv_tree_budget.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
+    L.tv_tree_budget.restype = i32
     L.tv_kv_commit.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
     L.tv_kv_commit.restype = i32
     _lib = L
@@ -260,3 +263,17 @@ def tv_kv_commit(k_cache, v_cache, ctx_len, accept_len, accepted_nodes, new_ctx_
                         _stream(k_cache.device))
     _check(st, "tv_kv_commit")
     return new_ctx_len
+
+
+def tv_tree_budget(score, n_nodes, cost, n_nodes_out=None):
+    """score [b][N] f64, n_nodes [b], cost [>= N] f64 -> n_nodes_out [b] (the
+    best-first prefix maximising (1 + S_n) / cost[n], plus the root)."""
+    L = _load()
+    b, N = score.shape
+    if n_nodes_out is None:
+        n_nodes_out = torch.empty((b,), dtype=torch.int32, device=score.device)
+    st = L.tv_tree_budget(_dev(score, "score", torch.float64), _dev(n_nodes, "n_nodes", torch.int32),
+                          _dev(cost, "cost", torch.float64), b, N, cost.numel(),
+                          _dev(n_nodes_out, "n_nodes_out", torch.int32), _stream(score.device))
+    _check(st, "tv_tree_budget")
+    return n_nodes_out

@@ -169,6 +169,16 @@ tv_status tv_tree_accept(const void* target_logits, const void* draft_logits, tv
 }
 
 // ---------------------------------------------------------------------------
+tv_status tv_tree_budget(const double* score, const int32_t* n_nodes, const double* cost,
+                         int batch, int N, int ncost, int32_t* n_nodes_out, hipStream_t stream) {
+  if (!score || !n_nodes || !cost || !n_nodes_out) return TV_ERR_INVALID;
+  if (batch < 1 || N < 1 || ncost < N) return TV_ERR_INVALID;
+  if (N > 1024 || batch > 0x7fffffff) return TV_ERR_UNSUPPORTED;
+  return device_status(
+      tvk::launch_tree_budget(score, n_nodes, cost, batch, N, n_nodes_out, stream));
+}
+
+// ---------------------------------------------------------------------------
 tv_status tv_kv_commit(void* k_cache, void* v_cache, tv_dtype dt, int batch, int Hkv, int cap,
                        int D, const int32_t* ctx_len, const int32_t* accept_len,
                        const int32_t* accepted_nodes, int width, int32_t* new_ctx_len,

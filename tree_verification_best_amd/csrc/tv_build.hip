@@ -557,6 +557,62 @@ __global__ __launch_bounds__(NT) void k_ancestors(const int* __restrict__ parent
 }
 
 // ---------------------------------------------------------------------------
+// cost-aware tree size (TAPS sec. 3.2 and sec. 4.1, third stage): keep the
+// best-first prefix of n* draft nodes, n* = the smallest n maximising
+// (1 + S_n) / c[n], S_n = s_1 + ... + s_n summed left to right in fp64.
+// One wave per sequence: the prefix sums are made in order (a uniform
+// chain over the lanes' scores), then each lane rates its sizes and the
+// best is found over the lanes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(WAVE) void k_tree_budget(const double* __restrict__ score,
+                                                     const int* __restrict__ n_nodes,
+                                                     const double* __restrict__ cost, int N,
+                                                     int* n_out) {
+  __shared__ double S[1024];
+  const int b = blockIdx.x, lane = lane_id();
+  const int n = n_nodes[b];
+  if (n < 1 || n > N) {
+    if (lane == 0) n_out[b] = n;
+    return;
+  }
+  double run = 0.0;
+  if (lane == 0) S[0] = 0.0;
+  for (int i0 = 1; i0 < n; i0 += WAVE) {
+    const double x = i0 + lane < n ? score[(int64_t)b * N + i0 + lane] : 0.0;
+    const int m = min(WAVE, n - i0);
+    double mine = 0.0;
+    for (int j = 0; j < m; ++j) {
+      run = run + readlane_d(x, j);
+      if (lane == j) mine = run;
+    }
+    if (lane < m) S[i0 + lane] = mine;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  double best_r = -1.0;
+  int best_n = 0x7fffffff;
+  for (int m = lane; m < n; m += WAVE) {
+    const double r = (1.0 + S[m]) / cost[m];
+    if (r > best_r) {  // ascending m: the smallest size wins a tie
+      best_r = r;
+      best_n = m;
+    }
+  }
+  double br = readlane_d(best_r, 0);
+  int bn = readlane_i(best_n, 0);
+  for (int j = 1; j < WAVE; ++j) {
+    const double r = readlane_d(best_r, j);
+    const int m = readlane_i(best_n, j);
+    if (r > br || (r == br && m < bn)) {
+      br = r;
+      bn = m;
+    }
+  }
+  if (lane == 0) n_out[b] = bn + 1;
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 BuildPlan build_plan(int batch, int K, int V, int topk, int budget) {
@@ -629,6 +685,13 @@ hipError_t launch_build(const BuildPlan& p, const void* draft, bool bf16, int ba
   else
     TV_SELECT(1024);
 #undef TV_SELECT
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_budget(const double* score, const int* n_nodes, const double* cost,
+                              int batch, int N, int* n_out, hipStream_t stream) {
+  hipLaunchKernelGGL(k_tree_budget, dim3(batch), dim3(WAVE), 0, stream, score, n_nodes, cost, N,
+                     n_out);
   return hipGetLastError();
 }
 

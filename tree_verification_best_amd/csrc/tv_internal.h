@@ -32,6 +32,8 @@ hipError_t launch_build(const BuildPlan& p, const void* draft, bool bf16, int ba
                         const int* ctx_len, int* parent, int* token, int* depth, int* pos,
                         double* score, uint64_t* anc, int* n_nodes, void* ws,
                         hipStream_t stream);
+hipError_t launch_tree_budget(const double* score, const int* n_nodes, const double* cost,
+                              int batch, int N, int* n_out, hipStream_t stream);
 hipError_t launch_ancestors(const int* parent, const int* n_nodes, const int* ctx_len,
                             int batch, int N, int* depth, int* pos, uint64_t* anc,
                             hipStream_t stream);
