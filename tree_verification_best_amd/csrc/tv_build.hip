@@ -570,6 +570,8 @@ __global__ __launch_bounds__(WAVE) void k_tree_budget(const double* __restrict__
                                                      int* n_out) {
   __shared__ double S[1024];
   const int b = blockIdx.x, lane = lane_id();
+  // the first 64 scores (every row below N exists) travel with n_nodes
+  const double x0 = 1 + lane < N ? score[(int64_t)b * N + 1 + lane] : 0.0;
   const int n = n_nodes[b];
   if (n < 1 || n > N) {
     if (lane == 0) n_out[b] = n;
@@ -578,7 +580,7 @@ __global__ __launch_bounds__(WAVE) void k_tree_budget(const double* __restrict__
   double run = 0.0;
   if (lane == 0) S[0] = 0.0;
   for (int i0 = 1; i0 < n; i0 += WAVE) {
-    const double x = i0 + lane < n ? score[(int64_t)b * N + i0 + lane] : 0.0;
+    const double x = i0 == 1 ? x0 : (i0 + lane < n ? score[(int64_t)b * N + i0 + lane] : 0.0);
     const int m = min(WAVE, n - i0);
     double mine = 0.0;
     for (int j = 0; j < m; ++j) {
