@@ -226,3 +226,4 @@ def tree_accept(target, parent, token, depth, n_nodes, *, mode, temperature=1.0,
 from .attention import tree_attention, tree_attention_rows  # noqa: E402,F401
 from .commit import kv_commit  # noqa: E402,F401
 from .budget import tree_budget  # noqa: E402,F401
+from .expand import tree_expand, tree_root  # noqa: E402,F401
