@@ -2,9 +2,11 @@
 
 A step is the whole round on one batch of synthetic input already resident in
 HBM: tv_tree_build -> tv_tree_attention_verify (one layer) -> tv_tree_accept.
-The KV commit that closes a round (tv_kv_commit) and the cost-aware tree size
-(tv_tree_budget) are timed after the steps, as replays of captured graphs, and
-reported as per_call.commit and per_call.budget.
+The KV commit that closes a round (tv_kv_commit), the cost-aware tree size
+(tv_tree_budget) and a layer-wise build of the same capacity (tv_tree_root +
+K drafting steps of tv_tree_expand, frontier width 8) are timed after the
+steps, as replays of captured graphs, and reported as per_call.commit,
+per_call.budget and per_call.expand (one drafting step).
 The default workload is the 4B-class GQA layer (32 query / 8 KV heads, head
 dim 128, bf16, context 4096, K = 16 draft positions, top-8, budget 64,
 vocabulary 151936, sampled acceptance at T = 1).  Inputs rotate over enough
@@ -35,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+EXPAND_W = 8   # frontier width of the layer-wise build timed beside the round
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -348,6 +351,41 @@ def main():
         c1.record(stream)
         torch.cuda.synchronize()
         calls["budget"] = c0.elapsed_time(c1) / (reps * ncommit)
+        # a layer-wise build of the same tree capacity: tv_tree_root, then K
+        # drafting steps of tv_tree_expand at a frontier of EXPAND_W slots with
+        # top-k children, on the drafter's next-token logits (the same dtype
+        # as the draft marginals); per_call.expand is one step (the root
+        # call's share included)
+        xl = [torch.from_numpy(a).to(dev) for a in
+              workloads.expand_logits(dict(c, dtype="f32"), b, EXPAND_W, K)]
+        xtree = {f: torch.empty_like(t) for f, t in tree.items()}
+        front = torch.empty((b, EXPAND_W), **i32)
+        nxt = torch.empty((b, EXPAND_W), **i32)
+        ws_x = torch.empty(tv.tree_expand_workspace(b, EXPAND_W, V, c["k"]), dtype=torch.uint8,
+                           device=dev)
+        f0 = torch.full((b, EXPAND_W), -1, **i32)
+        f0[:, 0] = 0
+
+        def layerwise_():
+            tv.tv_tree_root(sets[0]["roots"], sets[0]["ctx"], N, out=xtree)
+            front.copy_(f0)
+            for j in range(K):
+                tv.tv_tree_expand(xl[j], c["k"], front, xtree, sets[0]["ctx"],
+                                  next_frontier=nxt, workspace=ws_x)
+                front.copy_(nxt)
+
+        layerwise_()
+        xg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(xg):
+            layerwise_()
+        xg.replay()
+        torch.cuda.synchronize()
+        c0.record(stream)
+        for _ in range(reps):
+            xg.replay()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        calls["expand"] = c0.elapsed_time(c1) / (reps * K)
 
     # ---- accounting ------------------------------------------------------
     nn_h = tree["n_nodes"].cpu().numpy()
@@ -360,6 +398,11 @@ def main():
     moved = float(acc["accept_len"].clamp(min=0).sum().item())
     abytes["commit"] = int(2 * 2 * c["Hkv"] * c["D"] * el * moved)
     abytes["budget"] = b * N * 8 + N * 8 + b * 8   # scores and costs in, counts in and out
+    if "expand" in calls:
+        # one drafting step reads the frontier's logit rows once and writes
+        # up to EXPAND_W * k new rows (4 int32, one f64, the ancestor row)
+        new_rows = min(EXPAND_W * c["k"], N - 1)
+        abytes["expand"] = b * (EXPAND_W * V * 4 + new_rows * (16 + 8 + 8 * W) + EXPAND_W * 8)
     aflops = attention_flops(c, nn_h, dep_h, ctx0)
     rows = b * N * c["Hq"]
     rounds_per_s = 1e3 / ms_per_step

@@ -7,7 +7,10 @@
  *   tv_tree_attention_verify tree-masked attention of the target over
  *                            context + tree (one layer)
  *   tv_tree_accept           acceptance walk -> accepted path + one token
- * plus tv_tree_ancestors for trees that come from elsewhere.
+ * plus tv_tree_ancestors for trees that come from elsewhere, tv_tree_root and
+ * tv_tree_expand (a layer-wise builder: root, then one call per drafting
+ * step), tv_tree_budget (cost-aware tree
+ * size) and tv_kv_commit (keep the accepted path in the KV cache).
  *
  * Conventions shared by every call
  *   - Every array argument is a DEVICE pointer owned by the caller, dense
@@ -232,6 +235,61 @@ tv_status tv_tree_accept(const void *target_logits, const void *draft_logits, tv
                          uint64_t seed, uint64_t round, int max_depth, int32_t *accept_len,
                          int32_t *accepted_nodes, int32_t *out_tokens, void *workspace,
                          size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * tv_tree_root -- a tree of capacity N that holds only its root.
+ *
+ * TreeGraft sec. 3.1: the first drafting step expands the root alone (the
+ * last verified token, score 1).  Row 0 gets parent -1, root_token[b], depth
+ * 0, pos L_b = ctx_len[b], score 1.0 and ancestor bit 0; rows 1..N-1 get
+ * -1 / 0 as rows past n_nodes do in tv_tree_build; n_nodes[b] = 1.
+ *   parent, token, depth, pos int32 [batch][N]; score double [batch][N];
+ *   anc_mask uint64 [batch][N][ceil(N/64)]; n_nodes int32 [batch]
+ * Limits: 1 <= N <= 1024.
+ * ------------------------------------------------------------------------ */
+tv_status tv_tree_root(const int32_t *root_token, const int32_t *ctx_len, int batch, int N,
+                       int32_t *parent, int32_t *token, int32_t *depth, int32_t *pos,
+                       double *score, uint64_t *anc_mask, int32_t *n_nodes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * tv_tree_expand -- one drafting step of a layer-wise tree builder.
+ *
+ * TreeGraft sec. 3.1 (standard single-drafter expansion): each step takes
+ * the frontier, the W best nodes added by the previous step by path score
+ * (the root alone at the first step); the drafter's next-token distribution
+ * at each frontier node gives its top-m tokens as children; an edge's score
+ * is the drafter's probability of the child's token and a node's score the
+ * product of the edge scores from the root.  The drafter runs outside this
+ * library: node_logits holds its next-token logits at each frontier slot.
+ *
+ * Per sequence b with n0 = n_nodes[b]: the children of the valid frontier
+ * slots (row in [0, n0)) are appended in slot order, then rank order
+ * ((q desc, id asc), q = W / Z at build_temp as in tv_tree_build), at rows
+ * n0, n0 + 1, ...; rows from N on are dropped.  A child c of parent f gets
+ * parent f, its token, depth[f] + 1, pos = L_b + depth, score
+ * fl64(score[f] * q) and anc_mask row anc[f] | bit c.  n_nodes[b] becomes
+ * the new count and next_frontier[b] the W new rows of highest score (ties:
+ * lower row first), padded with -1: it is the frontier of the next step.
+ * A sequence with n0 outside [1, N] is left as it is (next_frontier all -1).
+ *   node_logits   [batch][W][V], dtype dt (f32 or bf16); rows of empty
+ *                 slots are read but unused
+ *   ctx_len       [batch]
+ *   frontier      int32 [batch][W] rows of the tree, -1 for an empty slot
+ *   parent, token, depth, pos, score, anc_mask, n_nodes   a tree as written
+ *                 by tv_tree_build (capacity N rows), updated in place
+ *   next_frontier int32 [batch][W], may be the frontier array itself
+ * Start from tv_tree_root's root-only tree and frontier {0, -1, ...};
+ * repeat with the drafter's logits at next_frontier.
+ * Limits: 1 <= W <= 64, 1 <= m <= min(64, V), V <= 2^18, W * m <= 4096,
+ *   1 <= N <= 1024, build_temp > 0.
+ * ------------------------------------------------------------------------ */
+size_t tv_tree_expand_workspace(int batch, int W, int V, int m);
+tv_status tv_tree_expand(const void *node_logits, tv_dtype dt, int batch, int W, int V, int m,
+                         float build_temp, const int32_t *ctx_len, const int32_t *frontier,
+                         int N, int32_t *parent, int32_t *token, int32_t *depth, int32_t *pos,
+                         double *score, uint64_t *anc_mask, int32_t *n_nodes,
+                         int32_t *next_frontier, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * tv_tree_budget -- cost-aware size of the tree to verify.

@@ -16,7 +16,8 @@ order, at rows n_nodes, n_nodes + 1, ...; rows past the tree's capacity N are
 dropped.  Each child gets depth(parent) + 1, pos = L + depth, its ancestor
 row (the parent's plus itself) and s = fl64(s(parent) * q).  The next frontier
 is the W new children with the highest s (ties: the lower row), padded
-with -1.  A frontier slot holding -1 or a row outside [0, n_nodes) is empty.
+with -1.  A frontier slot holding -1 or a row outside [0, n_nodes) is empty;
+a sequence whose n_nodes is outside [1, N] is left as it is.
 """
 import numpy as np
 
@@ -33,6 +34,8 @@ def tree_expand(node_logits, m, frontier, tree, ctx_len, build_temp=1.0):
     nxt = np.full((b, W), -1, np.int32)
     for s in range(b):
         n0 = int(t["n_nodes"][s])
+        if n0 < 1 or n0 > N:  # not a tree: left as it is
+            continue
         tok, q, _ = draft_candidates(node_logits[s], m, build_temp)
         row = n0
         new = []

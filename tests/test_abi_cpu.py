@@ -20,7 +20,7 @@ def _declared():
 
 def test_header_functions_exported():
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 14
     lib = ctypes.CDLL(tv.LIBPATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -50,6 +50,9 @@ def test_workspace_queries():
     s = L.tv_tree_accept_workspace(1, 65, 16, 151936, tv.TV_SAMPLED, 0)
     d = L.tv_tree_accept_workspace(1, 65, 16, 151936, tv.TV_SAMPLED, 1)
     assert g < s < d
+    assert L.tv_tree_expand_workspace(1, 8, 151936, 8) > 0
+    assert L.tv_tree_expand_workspace(1, 65, 100, 4) == 0    # W > 64
+    assert L.tv_tree_expand_workspace(1, 8, 100, 101) == 0   # m > V
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
@@ -187,3 +190,41 @@ def test_budget_rejects():
     assert L.tv_tree_budget(FAKE, FAKE, FAKE, 1, 8, 7, FAKE, None) == tv.TV_ERR_INVALID  # ncost < N
     assert L.tv_tree_budget(FAKE, FAKE, FAKE, 0, 8, 8, FAKE, None) == tv.TV_ERR_INVALID
     assert L.tv_tree_budget(FAKE, FAKE, FAKE, 1, 1025, 2000, FAKE, None) == tv.TV_ERR_UNSUPPORTED
+
+
+def test_root_rejects():
+    L = tv.lib()
+    f = [FAKE] * 7
+    assert L.tv_tree_root(None, FAKE, 1, 8, *f, None) == tv.TV_ERR_INVALID
+    assert L.tv_tree_root(FAKE, FAKE, 0, 8, *f, None) == tv.TV_ERR_INVALID
+    assert L.tv_tree_root(FAKE, FAKE, 1, 0, *f, None) == tv.TV_ERR_INVALID
+    assert L.tv_tree_root(FAKE, FAKE, 1, 1025, *f, None) == tv.TV_ERR_UNSUPPORTED
+
+
+def _expand(**kw):
+    a = dict(x=FAKE, dt=0, batch=1, W=4, V=100, m=4, temp=1.0, ctx=FAKE, front=FAKE, N=64,
+             nxt=FAKE, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return tv.lib().tv_tree_expand(a["x"], a["dt"], a["batch"], a["W"], a["V"], a["m"],
+                                   a["temp"], a["ctx"], a["front"], a["N"], *([FAKE] * 7),
+                                   a["nxt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), tv.TV_ERR_INVALID),
+    (dict(nxt=None), tv.TV_ERR_INVALID),
+    (dict(dt=3), tv.TV_ERR_INVALID),
+    (dict(temp=0.0), tv.TV_ERR_INVALID),
+    (dict(temp=float("nan")), tv.TV_ERR_INVALID),
+    (dict(W=0), tv.TV_ERR_INVALID),
+    (dict(m=101), tv.TV_ERR_INVALID),
+    (dict(N=0), tv.TV_ERR_INVALID),
+    (dict(W=65), tv.TV_ERR_UNSUPPORTED),
+    (dict(m=65), tv.TV_ERR_UNSUPPORTED),
+    (dict(N=1025), tv.TV_ERR_UNSUPPORTED),
+    (dict(V=1 << 19), tv.TV_ERR_UNSUPPORTED),
+    (dict(wsb=16), tv.TV_ERR_WORKSPACE),
+    (dict(ws=None), tv.TV_ERR_WORKSPACE),
+])
+def test_expand_rejects(kw, status):
+    assert _expand(**kw) == status

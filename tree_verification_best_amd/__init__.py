@@ -12,6 +12,8 @@ raise.
     tv_tree_ancestors        depth / positions / ancestor rows of a parent array
     tv_tree_attention_verify tree-masked GQA attention over context + tree
     tv_tree_accept           greedy or sampled acceptance walk
+    tv_tree_root             a root-only tree (start of a layer-wise build)
+    tv_tree_expand           one drafting step of a layer-wise (Top_W) builder
     tv_tree_budget           cost-aware tree size (best-first prefix)
     tv_kv_commit             keep the accepted path in the KV cache
 """
@@ -31,7 +33,8 @@ TV_PROPOSAL_POINT_MASS, TV_PROPOSAL_DRAFT = 0, 1
 
 EXPORTS = ("tv_status_string", "tv_version", "tv_tree_build_workspace", "tv_tree_build",
            "tv_tree_ancestors", "tv_tree_attention_workspace", "tv_tree_attention_verify",
-           "tv_tree_accept_workspace", "tv_tree_accept", "tv_tree_budget", "tv_kv_commit")
+           "tv_tree_accept_workspace", "tv_tree_accept", "tv_tree_budget", "tv_kv_commit",
+           "tv_tree_root", "tv_tree_expand_workspace", "tv_tree_expand")
 
 _lib = None
 
@@ -78,6 +81,13 @@ def _load():
     L.tv_tree_budget.restype = i32
     L.tv_kv_commit.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
     L.tv_kv_commit.restype = i32
+    L.tv_tree_root.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.tv_tree_root.restype = i32
+    L.tv_tree_expand_workspace.argtypes = [i32, i32, i32, i32]
+    L.tv_tree_expand_workspace.restype = sz
+    L.tv_tree_expand.argtypes = [vp, i32, i32, i32, i32, i32, f32, vp, vp, i32, vp, vp, vp, vp,
+                                 vp, vp, vp, vp, vp, sz, vp]
+    L.tv_tree_expand.restype = i32
     _lib = L
     return L
 
@@ -277,3 +287,63 @@ def tv_tree_budget(score, n_nodes, cost, n_nodes_out=None):
                           _dev(n_nodes_out, "n_nodes_out", torch.int32), _stream(score.device))
     _check(st, "tv_tree_budget")
     return n_nodes_out
+
+
+def tree_expand_workspace(batch, W, V, m):
+    return _load().tv_tree_expand_workspace(batch, W, V, m)
+
+
+def tv_tree_root(root_token, ctx_len, N, out=None):
+    """A batch of trees of capacity N holding only their roots (row 0)."""
+    L = _load()
+    b = root_token.shape[0]
+    dev = root_token.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    if out is None:
+        out = dict(parent=torch.empty((b, N), **i32), token=torch.empty((b, N), **i32),
+                   depth=torch.empty((b, N), **i32), pos=torch.empty((b, N), **i32),
+                   score=torch.empty((b, N), dtype=torch.float64, device=dev),
+                   anc=torch.empty((b, N, (N + 63) // 64), dtype=torch.int64, device=dev),
+                   n_nodes=torch.empty((b,), **i32))
+    if tuple(out["anc"].shape) != (b, N, (N + 63) // 64):
+        raise ValueError("anc must be [b][N][ceil(N/64)]")
+    st = L.tv_tree_root(_dev(root_token, "root_token", torch.int32),
+                        _dev(ctx_len, "ctx_len", torch.int32), b, N, _dev(out["parent"], "parent"),
+                        _dev(out["token"], "token"), _dev(out["depth"], "depth"),
+                        _dev(out["pos"], "pos"), _dev(out["score"], "score"),
+                        _dev(out["anc"], "anc"), _dev(out["n_nodes"], "n_nodes"), _stream(dev))
+    _check(st, "tv_tree_root")
+    return out
+
+
+def tv_tree_expand(node_logits, m, frontier, tree, ctx_len, build_temp=1.0,
+                   next_frontier=None, workspace=None):
+    """One drafting step: node_logits [b][W][V] (f32/bf16) at the frontier
+    rows frontier [b][W]; tree (dict as from tv_tree_build) is extended in
+    place.  Returns next_frontier [b][W] (may be `frontier` itself)."""
+    L = _load()
+    b, W, V = node_logits.shape
+    N = tree["parent"].shape[1]
+    dev = node_logits.device
+    if tuple(frontier.shape) != (b, W):
+        raise ValueError("frontier must be [b][W]")
+    if tuple(tree["anc"].shape) != (b, N, (N + 63) // 64):
+        raise ValueError("anc must be [b][N][ceil(N/64)]")
+    if next_frontier is None:
+        next_frontier = torch.empty((b, W), dtype=torch.int32, device=dev)
+    need = L.tv_tree_expand_workspace(b, W, V, m)
+    ws, wsb = _workspace(need, dev, workspace)
+    st = L.tv_tree_expand(_dev(node_logits, "node_logits"), _dt(node_logits), b, W, V, m,
+                          float(build_temp), _dev(ctx_len, "ctx_len", torch.int32),
+                          _dev(frontier, "frontier", torch.int32), N,
+                          _dev(tree["parent"], "parent", torch.int32),
+                          _dev(tree["token"], "token", torch.int32),
+                          _dev(tree["depth"], "depth", torch.int32),
+                          _dev(tree["pos"], "pos", torch.int32),
+                          _dev(tree["score"], "score", torch.float64),
+                          _dev(tree["anc"], "anc", torch.int64),
+                          _dev(tree["n_nodes"], "n_nodes", torch.int32),
+                          _dev(next_frontier, "next_frontier", torch.int32),
+                          ws.data_ptr(), wsb, _stream(dev))
+    _check(st, "tv_tree_expand")
+    return next_frontier

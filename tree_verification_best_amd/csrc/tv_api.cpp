@@ -82,6 +82,45 @@ tv_status tv_tree_build(const void* draft_logits, tv_dtype dt, int batch, int K,
                                          stream));
 }
 
+tv_status tv_tree_root(const int32_t* root_token, const int32_t* ctx_len, int batch, int N,
+                       int32_t* parent, int32_t* token, int32_t* depth, int32_t* pos,
+                       double* score, uint64_t* anc_mask, int32_t* n_nodes, hipStream_t stream) {
+  if (!root_token || !ctx_len || !parent || !token || !depth || !pos || !score || !anc_mask ||
+      !n_nodes)
+    return TV_ERR_INVALID;
+  if (batch < 1 || N < 1) return TV_ERR_INVALID;
+  if (N > 1024) return TV_ERR_UNSUPPORTED;
+  return device_status(tvk::launch_tree_root(root_token, ctx_len, batch, N, parent, token, depth,
+                                             pos, score, anc_mask, n_nodes, stream));
+}
+
+size_t tv_tree_expand_workspace(int batch, int W, int V, int m) {
+  if (!build_args_ok(batch, W, V, m, 0)) return 0;
+  return tvk::build_plan(batch, W, V, m, 0).workspace;
+}
+
+tv_status tv_tree_expand(const void* node_logits, tv_dtype dt, int batch, int W, int V, int m,
+                         float build_temp, const int32_t* ctx_len, const int32_t* frontier,
+                         int N, int32_t* parent, int32_t* token, int32_t* depth, int32_t* pos,
+                         double* score, uint64_t* anc_mask, int32_t* n_nodes,
+                         int32_t* next_frontier, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (!node_logits || !ctx_len || !frontier || !parent || !token || !depth || !pos || !score ||
+      !anc_mask || !n_nodes || !next_frontier)
+    return TV_ERR_INVALID;
+  if (dt != TV_F32 && dt != TV_BF16) return TV_ERR_INVALID;
+  if (!finite_pos(build_temp)) return TV_ERR_INVALID;
+  if (batch < 1 || W < 1 || V < 1 || m < 1 || m > V || N < 1) return TV_ERR_INVALID;
+  if (!build_args_ok(batch, W, V, m, 0) || N > 1024) return TV_ERR_UNSUPPORTED;
+  const tvk::BuildPlan p = tvk::build_plan(batch, W, V, m, 0);
+  if (p.C * m > 256 * tvk::kFinalizeE || p.rows > kMaxGridY) return TV_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < p.workspace) return TV_ERR_WORKSPACE;
+  return device_status(tvk::launch_tree_expand(p, node_logits, dt == TV_BF16, batch, W, V, m,
+                                               1.0f / build_temp, N, ctx_len, frontier, parent,
+                                               token, depth, pos, score, anc_mask, n_nodes,
+                                               next_frontier, workspace, stream));
+}
+
 tv_status tv_tree_ancestors(const int32_t* parent, const int32_t* n_nodes,
                             const int32_t* ctx_len, int batch, int N, int32_t* depth,
                             int32_t* pos, uint64_t* anc_mask, hipStream_t stream) {

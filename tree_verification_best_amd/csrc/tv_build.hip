@@ -614,6 +614,106 @@ __global__ __launch_bounds__(WAVE) void k_tree_budget(const double* __restrict__
   if (lane == 0) n_out[b] = bn + 1;
 }
 
+// A tree of capacity N holding only its root (row 0), in the row layout of
+// the build: the start of a layer-wise build.
+__global__ __launch_bounds__(kBuildNT) void k_tree_root(
+    const int* __restrict__ root_token, const int* __restrict__ ctx_len, int N,
+    int* __restrict__ parent, int* __restrict__ token, int* __restrict__ depth,
+    int* __restrict__ pos, double* __restrict__ score, uint64_t* __restrict__ anc,
+    int* __restrict__ n_nodes) {
+  const int b = blockIdx.x;
+  const int Wd = (N + 63) / 64;
+  const int64_t rb = (int64_t)b * N;
+  const int tk = root_token[b], L = ctx_len[b];
+  for (int i = threadIdx.x; i < N; i += kBuildNT) {
+    const bool root = i == 0;
+    parent[rb + i] = -1;
+    token[rb + i] = root ? tk : -1;
+    depth[rb + i] = root ? 0 : -1;
+    pos[rb + i] = root ? L : -1;
+    score[rb + i] = root ? 1.0 : 0.0;
+  }
+  for (int e = threadIdx.x; e < N * Wd; e += kBuildNT) anc[rb * Wd + e] = e == 0 ? 1ull : 0ull;
+  if (threadIdx.x == 0) n_nodes[b] = 1;
+}
+
+// ---------------------------------------------------------------------------
+// Layer-wise frontier expansion (TreeGraft sec. 3.1, standard single-drafter
+// expansion): the candidates of each frontier slot (top-m of its next-token
+// row, q desc) become children appended in slot, then rank order; the next
+// frontier is the W best new rows by (score desc, row asc), found by
+// counting.  Parents are existing rows, children new rows, so no row is both
+// read and written.
+// ---------------------------------------------------------------------------
+template <int NT>
+__global__ __launch_bounds__(NT) void k_expand(
+    const int* __restrict__ ftok, const double* __restrict__ fq, int W, int m, int N,
+    const int* __restrict__ ctx_len, const int* __restrict__ frontier, int* __restrict__ parent,
+    int* __restrict__ token, int* __restrict__ depth, int* __restrict__ pos,
+    double* __restrict__ score, uint64_t* __restrict__ anc, int* __restrict__ n_nodes,
+    int* __restrict__ next_frontier) {
+  __shared__ int s_base[64], s_node[64];
+  __shared__ int s_valid;
+  __shared__ double s_new[1024];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id();
+  const int n0 = n_nodes[b];
+  const int Wd = (N + 63) / 64;
+  const int64_t rb = (int64_t)b * N;
+  if (n0 < 1 || n0 > N) {  // not a tree: left as it is
+    for (int w = tid; w < W; w += NT) next_frontier[(int64_t)b * W + w] = -1;
+    return;
+  }
+  if (tid < WAVE) {
+    const int f = tid < W ? frontier[(int64_t)b * W + tid] : -1;
+    const bool ok = f >= 0 && f < n0;
+    const uint64_t bal = __ballot(ok);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    s_base[tid] = ok ? n0 + before * m : -1;
+    s_node[tid] = f;
+    if (tid == 0) s_valid = __popcll(bal);
+  }
+  __syncthreads();
+  const int n1 = min(N, n0 + s_valid * m);
+  const int L = ctx_len[b];
+  for (int e = tid; e < W * m; e += NT) {
+    const int w = e / m, r = e - w * m;
+    const int base = s_base[w];
+    if (base < 0 || base + r >= N) continue;
+    const int row = base + r, f = s_node[w];
+    const int64_t ci = ((int64_t)b * W + w) * m + r;
+    const double sc = score[rb + f] * fq[ci];
+    const int d = depth[rb + f] + 1;
+    parent[rb + row] = f;
+    token[rb + row] = ftok[ci];
+    depth[rb + row] = d;
+    pos[rb + row] = L + d;
+    score[rb + row] = sc;
+    for (int j = 0; j < Wd; ++j)
+      anc[(rb + row) * Wd + j] =
+          anc[(rb + f) * Wd + j] | (j == row / 64 ? 1ull << (row % 64) : 0ull);
+    s_new[row - n0] = sc;
+  }
+  __syncthreads();
+  const int nn = n1 - n0;
+  for (int e = tid; e < nn; e += NT) {
+    const double x = s_new[e];
+    int rank = 0;
+    for (int j0 = 0; j0 < nn; j0 += 8) {
+      double y[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) y[q] = s_new[min(j0 + q, nn - 1)];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = j0 + q;
+        rank += (j < nn && (y[q] > x || (y[q] == x && j < e))) ? 1 : 0;
+      }
+    }
+    if (rank < W) next_frontier[(int64_t)b * W + rank] = n0 + e;
+  }
+  for (int w = nn + tid; w < W; w += NT) next_frontier[(int64_t)b * W + w] = -1;
+  if (tid == 0) n_nodes[b] = n1;
+}
+
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
@@ -687,6 +787,49 @@ hipError_t launch_build(const BuildPlan& p, const void* draft, bool bf16, int ba
   else
     TV_SELECT(1024);
 #undef TV_SELECT
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_expand(const BuildPlan& p, const void* logits, bool bf16, int batch, int W,
+                              int V, int m, float inv_t, int N, const int* ctx_len,
+                              const int* frontier, int* parent, int* token, int* depth, int* pos,
+                              double* score, uint64_t* anc, int* n_nodes, int* next_frontier,
+                              void* ws, hipStream_t stream) {
+  char* w = static_cast<char*>(ws);
+  float* cval = reinterpret_cast<float*>(w + p.off_cval);
+  int* cid = reinterpret_cast<int*>(w + p.off_cid);
+  uint64_t* cz = reinterpret_cast<uint64_t*>(w + p.off_cz);
+  int* ftok = reinterpret_cast<int*>(w + p.off_ftok);
+  double* fq = reinterpret_cast<double*>(w + p.off_fq);
+  constexpr int E1 = kBuildChunk / kBuildNT;
+  const dim3 g1(p.C, (unsigned)p.rows);
+  // the frontier slots' rows take the place of the draft positions
+  if (bf16) {
+    const uint16_t* d = static_cast<const uint16_t*>(logits);
+    hipLaunchKernelGGL((k_chunk_topk<uint16_t, E1>), g1, dim3(kBuildNT), 0, stream, d, V, p.C,
+                       p.chunk, m, cval, cid);
+    hipLaunchKernelGGL((k_chunk_z<uint16_t>), g1, dim3(kBuildNT), 0, stream, d, V, p.C, p.chunk,
+                       m, inv_t, cval, cz);
+  } else {
+    const float* d = static_cast<const float*>(logits);
+    hipLaunchKernelGGL((k_chunk_topk<float, E1>), g1, dim3(kBuildNT), 0, stream, d, V, p.C,
+                       p.chunk, m, cval, cid);
+    hipLaunchKernelGGL((k_chunk_z<float>), g1, dim3(kBuildNT), 0, stream, d, V, p.C, p.chunk, m,
+                       inv_t, cval, cz);
+  }
+  hipLaunchKernelGGL((k_finalize<kFinalizeE>), dim3((unsigned)p.rows), dim3(kBuildNT), 0,
+                     stream, V, p.C, p.chunk, m, inv_t, cval, cid, cz, ftok, fq);
+  hipLaunchKernelGGL((k_expand<kBuildNT>), dim3(batch), dim3(kBuildNT), 0, stream, ftok, fq, W, m,
+                     N, ctx_len, frontier, parent, token, depth, pos, score, anc, n_nodes,
+                     next_frontier);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_root(const int* root_token, const int* ctx_len, int batch, int N,
+                            int* parent, int* token, int* depth, int* pos, double* score,
+                            uint64_t* anc, int* n_nodes, hipStream_t stream) {
+  hipLaunchKernelGGL(k_tree_root, dim3(batch), dim3(kBuildNT), 0, stream, root_token, ctx_len, N,
+                     parent, token, depth, pos, score, anc, n_nodes);
   return hipGetLastError();
 }
 

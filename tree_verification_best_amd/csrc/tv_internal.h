@@ -32,6 +32,14 @@ hipError_t launch_build(const BuildPlan& p, const void* draft, bool bf16, int ba
                         const int* ctx_len, int* parent, int* token, int* depth, int* pos,
                         double* score, uint64_t* anc, int* n_nodes, void* ws,
                         hipStream_t stream);
+hipError_t launch_tree_expand(const BuildPlan& p, const void* logits, bool bf16, int batch, int W,
+                              int V, int m, float inv_t, int N, const int* ctx_len,
+                              const int* frontier, int* parent, int* token, int* depth, int* pos,
+                              double* score, uint64_t* anc, int* n_nodes, int* next_frontier,
+                              void* ws, hipStream_t stream);
+hipError_t launch_tree_root(const int* root_token, const int* ctx_len, int batch, int N,
+                            int* parent, int* token, int* depth, int* pos, double* score,
+                            uint64_t* anc, int* n_nodes, hipStream_t stream);
 hipError_t launch_tree_budget(const double* score, const int* n_nodes, const double* cost,
                               int batch, int N, int* n_out, hipStream_t stream);
 hipError_t launch_ancestors(const int* parent, const int* n_nodes, const int* ctx_len,

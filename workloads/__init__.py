@@ -22,6 +22,10 @@ Distributions:
     among earlier nodes of depth < max_depth with fewer than max_children
     children; tokens are uniform; the parent's target row is raised by
     `plant` at the child's token, so that walks go past the root.
+  * Layer-wise drafting (one call per drafting step): the drafter's
+    next-token rows at the W frontier slots are beta + N(0, 1) with one
+    beta ~ N(0, sigma^2) per sequence, shared by all steps and slots, so the
+    top-m sets of different slots overlap as those of one context do.
   * sigma in "N(0, sigma)" is read as the standard deviation.
 """
 import numpy as np
@@ -50,7 +54,7 @@ def rng(cfg_name, stream, salt=0):
 
 
 STREAM_DRAFT, STREAM_TARGET, STREAM_Q, STREAM_K, STREAM_V, STREAM_TREE, STREAM_CTX, \
-    STREAM_ROOT = range(8)
+    STREAM_ROOT, STREAM_EXPAND = range(9)
 
 
 def round_bf16(x):
@@ -140,4 +144,17 @@ def plant(target, parent, token, n_nodes, boost):
             p = parent[s, i]
             if p >= 0:
                 out[s, p, token[s, i]] += np.float32(boost)
+    return out
+
+
+def expand_logits(cfg, batch, W, steps, salt=0):
+    """Drafter next-token logits for `steps` layer-wise drafting steps:
+    list of float32 [b][W][V] (bf16-representable for bf16 configurations)."""
+    V, sig = cfg["V"], cfg["sigma"]
+    r = rng(cfg["name"], STREAM_EXPAND, salt)
+    beta = r.standard_normal((batch, 1, V), dtype=np.float32) * np.float32(sig)
+    out = []
+    for _ in range(steps):
+        x = beta + r.standard_normal((batch, W, V), dtype=np.float32)
+        out.append(round_bf16(x) if cfg["dtype"] == "bf16" else x)
     return out
