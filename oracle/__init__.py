@@ -8,7 +8,9 @@ with the HIP library in ``tree_verification_best_amd`` and never imports it.
   candidates and their probabilities, best-first and exhaustive subtree
   selection, ancestor sets, the greedy and sampled acceptance walks and the
   Philox4x64-10 generator.
-* ``oracle.attention``: tree-masked attention in fp64 numpy.
+* ``oracle.attention``: tree-masked attention in fp64 numpy; ``oracle.rope``: the
+  same with rotary embedding at the tree position ids, and the commit that
+  rotates the kept keys.
 """
 import ctypes
 import os
@@ -227,3 +229,5 @@ from .attention import tree_attention, tree_attention_rows  # noqa: E402,F401
 from .commit import kv_commit  # noqa: E402,F401
 from .budget import tree_budget  # noqa: E402,F401
 from .expand import tree_expand, tree_root  # noqa: E402,F401
+from .rope import (inv_freq, kv_commit_rope, rope, tree_attention_rope,  # noqa: E402,F401
+                   tree_attention_rope_rows)

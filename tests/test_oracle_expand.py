@@ -88,3 +88,36 @@ def test_structure_frontier_and_capacity(W, m):
         np.testing.assert_array_equal(t["anc"][s, :n], anc)
         np.testing.assert_array_equal(t["depth"][s, :n], depth)
         np.testing.assert_array_equal(t["pos"][s, :n], ctx[s] + depth)
+
+
+def test_children_are_each_slots_top_m_in_slot_then_rank_order():
+    """Brute force per frontier slot: its children sit at consecutive rows in
+    slot order; their tokens are the m largest logits of the slot's row
+    (ties: lower id), in order; each edge score score(child)/score(parent)
+    is the fp64 softmax probability of the child's token."""
+    r = np.random.default_rng(11)
+    b, W, m, N, V, T = 3, 4, 5, 64, 80, 0.7
+    ctx = np.array([2, 9, 0])
+    t = oracle.tree_root(b, N, np.zeros(b, np.int32), ctx)
+    frontier = np.full((b, W), -1, np.int32)
+    frontier[:, 0] = 0
+    logits = (r.standard_normal((b, W, V)) * 2).astype(np.float32)
+    t, frontier = oracle.tree_expand(logits, m, frontier, t, ctx, build_temp=T)
+    frontier[1, 2] = -1                  # an empty slot in the middle
+    logits = np.round(r.standard_normal((b, W, V)) * 2).astype(np.float32)  # many ties
+    prev = t
+    t, _ = oracle.tree_expand(logits, m, frontier, t, ctx, build_temp=T)
+    for s in range(b):
+        row = int(prev["n_nodes"][s])
+        for w in range(W):
+            f = int(frontier[s, w])
+            if f < 0:
+                continue
+            order = sorted(range(V), key=lambda i: (-float(logits[s, w, i]), i))[:m]
+            p = _softmax64(logits[s, w], T)
+            for rk, tok in enumerate(order):
+                assert t["parent"][s, row] == f and t["token"][s, row] == tok, (s, w, rk)
+                e = t["score"][s, row] / t["score"][s, f]
+                assert abs(e - p[tok]) <= EDGE_RTOL * p[tok]
+                row += 1
+        assert row == int(t["n_nodes"][s])
