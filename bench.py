@@ -6,7 +6,9 @@ The KV commit that closes a round (tv_kv_commit), the cost-aware tree size
 (tv_tree_budget) and a layer-wise build of the same capacity (tv_tree_root +
 K drafting steps of tv_tree_expand, frontier width 8) are timed after the
 steps, as replays of captured graphs, and reported as per_call.commit,
-per_call.budget and per_call.expand (one drafting step).
+per_call.budget and per_call.expand (one drafting step).  The verification
+with the rotary embedding fused (tv_tree_attention_verify_rope, base 1e6) is
+timed per call after the steps and reported as per_call.attention_rope.
 The default workload is the 4B-class GQA layer (32 query / 8 KV heads, head
 dim 128, bf16, context 4096, K = 16 draft positions, top-8, budget 64,
 vocabulary 151936, sampled acceptance at T = 1).  Inputs rotate over enough
@@ -38,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 EXPAND_W = 8   # frontier width of the layer-wise build timed beside the round
+ROPE_BASE = 1e6   # rotary base of the fused-rotation verification timed beside the round
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -315,6 +318,22 @@ def main():
     if graphs is None:
         for name, (a, z) in (("build", (0, 1)), ("attention", (1, 2)), ("accept", (2, 3))):
             calls[name] = sum(evs[i][a].elapsed_time(evs[i][z]) for i in range(args.steps)) / args.steps
+    # verification with the rotary embedding fused (queries and tree keys
+    # turned at the tree's position ids), per call with events like the plain
+    # call, over the same input sets and the last step's tree
+    nrope = min(args.steps, 100)
+    rev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nrope)]
+    for i in range(nrope + 5):
+        s = sets[i % nsets]
+        if i >= 5:
+            rev[i - 5][0].record(stream)
+        tv.tv_tree_attention_verify(s["q"], s["k"], s["v"], s["ctx"], tree["anc"], tree["n_nodes"],
+                                    max_ctx, workspace=ws_a, out=attn_out, lse=lse,
+                                    pos=tree["pos"], rope_base=ROPE_BASE)
+        if i >= 5:
+            rev[i - 5][1].record(stream)
+    torch.cuda.synchronize()
+    calls["attention_rope"] = sum(e[0].elapsed_time(e[1]) for e in rev) / nrope
     # the commit, outside the timed steps (acc holds the last step's walk).
     # One call is shorter than the host's launch path, so the calls are
     # captured into a graph and the replays timed, as device time.
@@ -398,6 +417,7 @@ def main():
     moved = float(acc["accept_len"].clamp(min=0).sum().item())
     abytes["commit"] = int(2 * 2 * c["Hkv"] * c["D"] * el * moved)
     abytes["budget"] = b * N * 8 + N * 8 + b * 8   # scores and costs in, counts in and out
+    abytes["attention_rope"] = abytes["attention"] + b * N * 4   # plus the position ids
     if "expand" in calls:
         # one drafting step reads the frontier's logit rows once and writes
         # up to EXPAND_W * k new rows (4 int32, one f64, the ancestor row)
@@ -413,10 +433,11 @@ def main():
         gbs = abytes[name] / (ms * 1e-3) / 1e9
         per_call[name] = dict(ms=round(ms, 5), algorithmic_MB=round(abytes[name] / 1e6, 3),
                               GBps=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
-    if "attention" in calls:
-        tf = aflops / (calls["attention"] * 1e-3) / 1e12
-        per_call["attention"]["TFLOPs"] = round(tf, 2)
-        per_call["attention"]["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+    for name in ("attention", "attention_rope"):
+        if name in calls:
+            tf = aflops / (calls[name] * 1e-3) / 1e12
+            per_call[name]["TFLOPs"] = round(tf, 2)
+            per_call[name]["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
     if "attention" in calls:
         # the verification pass: HBM-bound below the ridge point, else MFMA
         ms = calls["attention"]

@@ -9,8 +9,9 @@
  *   tv_tree_accept           acceptance walk -> accepted path + one token
  * plus tv_tree_ancestors for trees that come from elsewhere, tv_tree_root and
  * tv_tree_expand (a layer-wise builder: root, then one call per drafting
- * step), tv_tree_budget (cost-aware tree
- * size) and tv_kv_commit (keep the accepted path in the KV cache).
+ * step), tv_tree_budget (cost-aware tree size), tv_kv_commit (keep the
+ * accepted path in the KV cache) and the rotary-embedding variants
+ * tv_tree_attention_verify_rope and tv_kv_commit_rope.
  *
  * Conventions shared by every call
  *   - Every array argument is a DEVICE pointer owned by the caller, dense
@@ -184,6 +185,35 @@ tv_status tv_tree_attention_verify(const void *q, const void *k_cache, const voi
                                    size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * tv_tree_attention_verify_rope -- the same attention with the rotary
+ * position embedding applied inside the kernel, at the tree's position ids.
+ *
+ * PTD sec. 3.1: a node's position encoding follows from the size of its
+ * ancestor set, so node i sits at pos[b][i] = L_b + depth(i), the position it
+ * would have in the plain sequence of the context and its root-to-node path.
+ * The rotary embedding (not defined by the pages; the standard one with the
+ * half-split pairing): dimension d < D/2 pairs with d + D/2 and the pair
+ * turns by pos * rope_base^(-2d/D) radians.  Cache convention: context rows
+ * [0, L_b) hold keys already rotated at their own positions (as
+ * tv_kv_commit_rope leaves them); tree rows L_b + i hold keys as the target's
+ * projection wrote them.  This call rotates every query row i and every tree
+ * key row i at pos[b][i] as it loads them, then computes
+ * tv_tree_attention_verify's result; q and the caches are not modified.
+ *   pos        int32 [batch][N] position ids (tv_tree_build's pos)
+ *   rope_base  finite, > 1 (e.g. 1e4, 1e6); other arguments as above.
+ * Rotated bf16 values are rounded to bf16 (nearest even) before the matrix
+ * products; angles are reduced in fp64 before fp32 sin/cos.
+ * ------------------------------------------------------------------------ */
+tv_status tv_tree_attention_verify_rope(const void *q, const void *k_cache, const void *v_cache,
+                                        tv_dtype dt, const int32_t *ctx_len,
+                                        const uint64_t *anc_mask, const int32_t *n_nodes,
+                                        const int32_t *pos, double rope_base, int batch, int N,
+                                        int Hq, int Hkv, int D, int cap, int max_ctx, float scale,
+                                        int splits, void *out, tv_dtype out_dt, float *lse,
+                                        void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * tv_tree_accept -- the acceptance walk over one tree per sequence.
  *
  * Primer, "acceptance and rejection": starting at the root, greedy mode
@@ -344,6 +374,22 @@ tv_status tv_kv_commit(void *k_cache, void *v_cache, tv_dtype dt, int batch, int
                        int D, const int32_t *ctx_len, const int32_t *accept_len,
                        const int32_t *accepted_nodes, int width, int32_t *new_ctx_len,
                        hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * tv_kv_commit_rope -- tv_kv_commit for caches verified with
+ * tv_tree_attention_verify_rope: the kept tree keys were not rotated yet, so
+ * each kept K row j = 0..accept_len[b] (the root included) is turned at the
+ * position of the row it lands on, L_b + j (its node's position id: the
+ * path's j-th node has depth j), and rounded to the cache dtype (bf16:
+ * nearest even).  V rows move as in tv_kv_commit.  After the call every row
+ * below new_ctx_len holds a rotated key, as the next round expects.
+ *   rope_base  finite, > 1, the value verification used; other arguments,
+ *   checks and results as tv_kv_commit.
+ * ------------------------------------------------------------------------ */
+tv_status tv_kv_commit_rope(void *k_cache, void *v_cache, tv_dtype dt, int batch, int Hkv,
+                            int cap, int D, const int32_t *ctx_len, const int32_t *accept_len,
+                            const int32_t *accepted_nodes, int width, double rope_base,
+                            int32_t *new_ctx_len, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,7 @@ def _declared():
 
 def test_header_functions_exported():
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 16
     lib = ctypes.CDLL(tv.LIBPATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -228,3 +228,40 @@ def _expand(**kw):
 ])
 def test_expand_rejects(kw, status):
     assert _expand(**kw) == status
+
+
+def _attn_rope(pos=FAKE, base=1e4, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dt=1, ctx=FAKE, anc=FAKE, n=FAKE, batch=1, N=17, Hq=4,
+             Hkv=2, D=128, cap=200, max_ctx=128, scale=0.1, splits=0, out=FAKE, odt=0,
+             lse=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return tv.lib().tv_tree_attention_verify_rope(
+        a["q"], a["k"], a["v"], a["dt"], a["ctx"], a["anc"], a["n"], pos, base, a["batch"],
+        a["N"], a["Hq"], a["Hkv"], a["D"], a["cap"], a["max_ctx"], a["scale"], a["splits"],
+        a["out"], a["odt"], a["lse"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pos=None), tv.TV_ERR_INVALID),
+    (dict(base=1.0), tv.TV_ERR_INVALID),
+    (dict(base=0.5), tv.TV_ERR_INVALID),
+    (dict(base=float("inf")), tv.TV_ERR_INVALID),
+    (dict(base=float("nan")), tv.TV_ERR_INVALID),
+    (dict(q=None), tv.TV_ERR_INVALID),
+    (dict(D=96), tv.TV_ERR_UNSUPPORTED),
+    (dict(wsb=8), tv.TV_ERR_WORKSPACE),
+])
+def test_attention_rope_rejects(kw, status):
+    assert _attn_rope(**kw) == status
+
+
+def test_commit_rope_rejects():
+    L = tv.lib()
+
+    def call(base=1e4, k=FAKE, D=128):
+        return L.tv_kv_commit_rope(k, FAKE, 1, 1, 2, 64, D, FAKE, FAKE, FAKE, 17, base, FAKE,
+                                   None)
+    assert call(base=1.0) == tv.TV_ERR_INVALID
+    assert call(base=float("nan")) == tv.TV_ERR_INVALID
+    assert call(k=None) == tv.TV_ERR_INVALID
+    assert call(D=96) == tv.TV_ERR_UNSUPPORTED

@@ -16,6 +16,9 @@ raise.
     tv_tree_expand           one drafting step of a layer-wise (Top_W) builder
     tv_tree_budget           cost-aware tree size (best-first prefix)
     tv_kv_commit             keep the accepted path in the KV cache
+    tv_tree_attention_verify_rope / tv_kv_commit_rope
+                             the same with the rotary embedding at the tree's
+                             position ids (pos / rope_base arguments)
 """
 import ctypes
 import math
@@ -34,7 +37,8 @@ TV_PROPOSAL_POINT_MASS, TV_PROPOSAL_DRAFT = 0, 1
 EXPORTS = ("tv_status_string", "tv_version", "tv_tree_build_workspace", "tv_tree_build",
            "tv_tree_ancestors", "tv_tree_attention_workspace", "tv_tree_attention_verify",
            "tv_tree_accept_workspace", "tv_tree_accept", "tv_tree_budget", "tv_kv_commit",
-           "tv_tree_root", "tv_tree_expand_workspace", "tv_tree_expand")
+           "tv_tree_root", "tv_tree_expand_workspace", "tv_tree_expand",
+           "tv_tree_attention_verify_rope", "tv_kv_commit_rope")
 
 _lib = None
 
@@ -81,6 +85,13 @@ def _load():
     L.tv_tree_budget.restype = i32
     L.tv_kv_commit.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
     L.tv_kv_commit.restype = i32
+    L.tv_tree_attention_verify_rope.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, c.c_double, i32,
+                                                i32, i32, i32, i32, i32, i32, f32, i32, vp, i32,
+                                                vp, vp, sz, vp]
+    L.tv_tree_attention_verify_rope.restype = i32
+    L.tv_kv_commit_rope.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, i32, c.c_double,
+                                    vp, vp]
+    L.tv_kv_commit_rope.restype = i32
     L.tv_tree_root.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     L.tv_tree_root.restype = i32
     L.tv_tree_expand_workspace.argtypes = [i32, i32, i32, i32]
@@ -196,11 +207,12 @@ def attention_workspace(batch, N, Hq, Hkv, D, max_ctx, splits=0):
 
 def tv_tree_attention_verify(q, k_cache, v_cache, ctx_len, anc_mask, n_nodes, max_ctx,
                              scale=None, splits=0, want_lse=True, workspace=None, out=None,
-                             lse=None, out_dtype=torch.float32):
+                             lse=None, out_dtype=torch.float32, pos=None, rope_base=None):
     """q [b][N][Hq][D]; caches [b][Hkv][cap][D] -> (out [b][N][Hq][D], lse [b][N][Hq]).
 
     out is fp32 by default (the accumulated result); bf16 inputs may ask for
-    out_dtype=torch.bfloat16."""
+    out_dtype=torch.bfloat16.  With pos [b][N] and rope_base the call is
+    tv_tree_attention_verify_rope (queries and tree keys rotated at pos)."""
     L = _load()
     b, N, Hq, D = q.shape
     Hkv, cap = k_cache.shape[1], k_cache.shape[2]
@@ -212,15 +224,25 @@ def tv_tree_attention_verify(q, k_cache, v_cache, ctx_len, anc_mask, n_nodes, ma
         lse = torch.empty((b, N, Hq), dtype=torch.float32, device=dev)
     need = L.tv_tree_attention_workspace(b, N, Hq, Hkv, D, int(max_ctx), int(splits))
     ws, wsb = _workspace(need, dev, workspace)
-    st = L.tv_tree_attention_verify(_dev(q, "q"), _dev(k_cache, "k_cache", q.dtype),
-                                    _dev(v_cache, "v_cache", q.dtype), _dt(q),
-                                    _dev(ctx_len, "ctx_len", torch.int32),
-                                    _dev(anc_mask, "anc_mask", torch.int64),
-                                    _dev(n_nodes, "n_nodes", torch.int32), b, N, Hq, Hkv, D, cap,
-                                    int(max_ctx), scale, int(splits), _dev(out, "out"), _dt(out),
-                                    _dev(lse, "lse", torch.float32) if lse is not None else None,
-                                    ws.data_ptr(), wsb, _stream(dev))
-    _check(st, "tv_tree_attention_verify")
+    head = (_dev(q, "q"), _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
+            _dt(q), _dev(ctx_len, "ctx_len", torch.int32), _dev(anc_mask, "anc_mask", torch.int64),
+            _dev(n_nodes, "n_nodes", torch.int32))
+    tail = (b, N, Hq, Hkv, D, cap, int(max_ctx), scale, int(splits), _dev(out, "out"), _dt(out),
+            _dev(lse, "lse", torch.float32) if lse is not None else None, ws.data_ptr(), wsb,
+            _stream(dev))
+    if pos is None:
+        if rope_base is not None:
+            raise ValueError("rope_base needs pos")
+        st = L.tv_tree_attention_verify(*head, *tail)
+        _check(st, "tv_tree_attention_verify")
+    else:
+        if rope_base is None:
+            raise ValueError("pos needs rope_base")
+        if tuple(pos.shape) != (b, N):
+            raise ValueError("pos must be [b][N]")
+        st = L.tv_tree_attention_verify_rope(*head, _dev(pos, "pos", torch.int32),
+                                             float(rope_base), *tail)
+        _check(st, "tv_tree_attention_verify_rope")
     return out, lse
 
 
@@ -258,20 +280,27 @@ def tv_tree_accept(target_logits, parent, token, depth, n_nodes, *, mode, max_de
     return out
 
 
-def tv_kv_commit(k_cache, v_cache, ctx_len, accept_len, accepted_nodes, new_ctx_len=None):
+def tv_kv_commit(k_cache, v_cache, ctx_len, accept_len, accepted_nodes, new_ctx_len=None,
+                 rope_base=None):
     """Moves the accepted path's K/V rows behind the context, in place; returns
-    new_ctx_len [b] (a new tensor unless one is given; ctx_len itself may be)."""
+    new_ctx_len [b] (a new tensor unless one is given; ctx_len itself may be).
+    With rope_base the call is tv_kv_commit_rope (kept keys rotated at the
+    rows they land on)."""
     L = _load()
     b, Hkv, cap, D = k_cache.shape
     if new_ctx_len is None:
         new_ctx_len = torch.empty((b,), dtype=torch.int32, device=k_cache.device)
-    st = L.tv_kv_commit(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache", k_cache.dtype),
-                        _dt(k_cache), b, Hkv, cap, D, _dev(ctx_len, "ctx_len", torch.int32),
-                        _dev(accept_len, "accept_len", torch.int32),
-                        _dev(accepted_nodes, "accepted_nodes", torch.int32),
-                        accepted_nodes.shape[1], _dev(new_ctx_len, "new_ctx_len", torch.int32),
-                        _stream(k_cache.device))
-    _check(st, "tv_kv_commit")
+    head = (_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache", k_cache.dtype), _dt(k_cache), b,
+            Hkv, cap, D, _dev(ctx_len, "ctx_len", torch.int32),
+            _dev(accept_len, "accept_len", torch.int32),
+            _dev(accepted_nodes, "accepted_nodes", torch.int32), accepted_nodes.shape[1])
+    tail = (_dev(new_ctx_len, "new_ctx_len", torch.int32), _stream(k_cache.device))
+    if rope_base is None:
+        st = L.tv_kv_commit(*head, *tail)
+        _check(st, "tv_kv_commit")
+    else:
+        st = L.tv_kv_commit_rope(*head, float(rope_base), *tail)
+        _check(st, "tv_kv_commit_rope")
     return new_ctx_len
 
 

@@ -15,6 +15,7 @@ constexpr size_t kMaxSelectLds = 64 * 1024;
 constexpr int kMaxGridY = 65535;
 
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
+bool rope_base_ok(double base) { return std::isfinite(base) && base > 1.0; }
 
 bool build_args_ok(int batch, int K, int V, int topk, int budget) {
   return batch >= 1 && K >= 1 && K <= TV_MAX_POSITIONS && V >= 1 && V <= TV_MAX_VOCAB &&
@@ -138,15 +139,15 @@ size_t tv_tree_attention_workspace(int batch, int N, int Hq, int Hkv, int D, int
   return tvk::attention_plan(batch, N, Hq, Hkv, D, max_ctx, splits).workspace;
 }
 
-tv_status tv_tree_attention_verify(const void* q, const void* k_cache, const void* v_cache,
-                                   tv_dtype dt, const int32_t* ctx_len,
-                                   const uint64_t* anc_mask, const int32_t* n_nodes,
-                                   int batch, int N, int Hq, int Hkv, int D, int cap,
-                                   int max_ctx, float scale, int splits, void* out,
-                                   tv_dtype out_dt, float* lse, void* workspace,
-                                   size_t workspace_bytes, hipStream_t stream) {
+static tv_status attention_impl(const void* q, const void* k_cache, const void* v_cache,
+                                tv_dtype dt, const int32_t* ctx_len, const uint64_t* anc_mask,
+                                const int32_t* n_nodes, const int32_t* pos, double rope_base,
+                                int batch, int N, int Hq, int Hkv, int D, int cap, int max_ctx,
+                                float scale, int splits, void* out, tv_dtype out_dt, float* lse,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !ctx_len || !anc_mask || !n_nodes || !out)
     return TV_ERR_INVALID;
+  if (pos && !rope_base_ok(rope_base)) return TV_ERR_INVALID;
   if (dt != TV_F32 && dt != TV_BF16) return TV_ERR_INVALID;
   if (out_dt != TV_F32 && out_dt != TV_BF16) return TV_ERR_INVALID;
   if (dt == TV_F32 && out_dt != TV_F32) return TV_ERR_UNSUPPORTED;
@@ -161,8 +162,35 @@ tv_status tv_tree_attention_verify(const void* q, const void* k_cache, const voi
   if (dt == TV_BF16 && (!workspace || workspace_bytes < p.workspace)) return TV_ERR_WORKSPACE;
   return device_status(tvk::launch_attention(p, q, k_cache, v_cache, dt == TV_BF16, ctx_len,
                                              anc_mask, n_nodes, batch, N, Hq, Hkv, D, cap,
-                                             max_ctx, scale, out, out_dt == TV_F32, lse,
-                                             workspace, stream));
+                                             max_ctx, scale, out, out_dt == TV_F32, lse, pos,
+                                             pos ? std::log2(rope_base) : 0.0, workspace,
+                                             stream));
+}
+
+tv_status tv_tree_attention_verify(const void* q, const void* k_cache, const void* v_cache,
+                                   tv_dtype dt, const int32_t* ctx_len,
+                                   const uint64_t* anc_mask, const int32_t* n_nodes,
+                                   int batch, int N, int Hq, int Hkv, int D, int cap,
+                                   int max_ctx, float scale, int splits, void* out,
+                                   tv_dtype out_dt, float* lse, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  return attention_impl(q, k_cache, v_cache, dt, ctx_len, anc_mask, n_nodes, nullptr, 0.0, batch,
+                        N, Hq, Hkv, D, cap, max_ctx, scale, splits, out, out_dt, lse, workspace,
+                        workspace_bytes, stream);
+}
+
+tv_status tv_tree_attention_verify_rope(const void* q, const void* k_cache, const void* v_cache,
+                                        tv_dtype dt, const int32_t* ctx_len,
+                                        const uint64_t* anc_mask, const int32_t* n_nodes,
+                                        const int32_t* pos, double rope_base, int batch, int N,
+                                        int Hq, int Hkv, int D, int cap, int max_ctx, float scale,
+                                        int splits, void* out, tv_dtype out_dt, float* lse,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  if (!pos) return TV_ERR_INVALID;
+  return attention_impl(q, k_cache, v_cache, dt, ctx_len, anc_mask, n_nodes, pos, rope_base,
+                        batch, N, Hq, Hkv, D, cap, max_ctx, scale, splits, out, out_dt, lse,
+                        workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -218,19 +246,38 @@ tv_status tv_tree_budget(const double* score, const int32_t* n_nodes, const doub
 }
 
 // ---------------------------------------------------------------------------
-tv_status tv_kv_commit(void* k_cache, void* v_cache, tv_dtype dt, int batch, int Hkv, int cap,
-                       int D, const int32_t* ctx_len, const int32_t* accept_len,
-                       const int32_t* accepted_nodes, int width, int32_t* new_ctx_len,
-                       hipStream_t stream) {
+static tv_status kv_commit_impl(void* k_cache, void* v_cache, tv_dtype dt, int batch, int Hkv,
+                                int cap, int D, const int32_t* ctx_len,
+                                const int32_t* accept_len, const int32_t* accepted_nodes,
+                                int width, bool rope, double rope_base, int32_t* new_ctx_len,
+                                hipStream_t stream) {
   if (!k_cache || !v_cache || !ctx_len || !accept_len || !accepted_nodes || !new_ctx_len)
     return TV_ERR_INVALID;
   if (dt != TV_F32 && dt != TV_BF16) return TV_ERR_INVALID;
   if (batch < 1 || Hkv < 1 || cap < 1 || width < 1) return TV_ERR_INVALID;
+  if (rope && !rope_base_ok(rope_base)) return TV_ERR_INVALID;
   if ((D != 64 && D != 128) || width > tvk::kCommitMaxWidth || batch > 0x7fffffff)
     return TV_ERR_UNSUPPORTED;
   return device_status(tvk::launch_kv_commit(k_cache, v_cache, dt == TV_BF16 ? 2 : 4, batch, Hkv,
                                              cap, D, ctx_len, accept_len, accepted_nodes, width,
-                                             new_ctx_len, stream));
+                                             new_ctx_len, rope, rope ? std::log2(rope_base) : 0.0,
+                                             stream));
+}
+
+tv_status tv_kv_commit(void* k_cache, void* v_cache, tv_dtype dt, int batch, int Hkv, int cap,
+                       int D, const int32_t* ctx_len, const int32_t* accept_len,
+                       const int32_t* accepted_nodes, int width, int32_t* new_ctx_len,
+                       hipStream_t stream) {
+  return kv_commit_impl(k_cache, v_cache, dt, batch, Hkv, cap, D, ctx_len, accept_len,
+                        accepted_nodes, width, false, 0.0, new_ctx_len, stream);
+}
+
+tv_status tv_kv_commit_rope(void* k_cache, void* v_cache, tv_dtype dt, int batch, int Hkv,
+                            int cap, int D, const int32_t* ctx_len, const int32_t* accept_len,
+                            const int32_t* accepted_nodes, int width, double rope_base,
+                            int32_t* new_ctx_len, hipStream_t stream) {
+  return kv_commit_impl(k_cache, v_cache, dt, batch, Hkv, cap, D, ctx_len, accept_len,
+                        accepted_nodes, width, true, rope_base, new_ctx_len, stream);
 }
 
 }  // extern "C"

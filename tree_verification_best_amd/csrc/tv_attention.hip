@@ -68,13 +68,14 @@ __device__ __forceinline__ void lds_barrier() {
 // XCD w % 8), so workgroup w takes item (w % 8) * per + w / 8: every XCD gets
 // a contiguous range of items, i.e. all the splits of a few (KV head, row
 // tile) pairs, and the Q rows and K/V of a head stay in one XCD's L2.
-template <int D>
+template <int D, bool ROPE>
 __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int* __restrict__ ctx_len,
     const uint64_t* __restrict__ anc, const int* __restrict__ n_nodes, int N, int Hq, int Hkv,
     int cap, int S, int KS, int MT, int items, float scale_log2, uint16_t* __restrict__ Opart,
-    float* __restrict__ Mpart, float* __restrict__ Lpart, int batch) {
+    float* __restrict__ Mpart, float* __restrict__ Lpart, int batch, const int* __restrict__ pos,
+    double log2_base) {
   constexpr int KP = D + 8;   // K tile pitch (bf16): 16-byte reads spread over banks
   constexpr int VP = D + 16;  // V tile pitch (bf16): the 16 rows of a transposing read
                               // (4 keys x 4 column groups) fall in distinct banks
@@ -83,6 +84,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
   __shared__ __align__(16) uint16_t Ks[kTileKeys * KP];
   __shared__ __align__(16) uint16_t Vs[kTileKeys * VP];
   __shared__ uint64_t Aw[kAttnWaves * 32 * 16];  // ancestor rows (tree split)
+  __shared__ double Rt[ROPE ? D / 2 : 1];         // rotary rate of each pair
+  __shared__ int Pk[ROPE ? 1024 : 1];             // position ids of the tree keys
 
   const int w = blockIdx.x;
   const int per = (items + 7) / 8;
@@ -128,6 +131,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
       qf[c] = __builtin_bit_cast(bf16x8, raw);
     }
   }
+  if constexpr (ROPE) {
+    // the rotary embedding at the tree position ids (pos[b][i] = L + depth):
+    // the lane's Q elements d = 16 c + 8 half + e hold both members of each
+    // pair (d, d + D/2), in chunks c and c + D/32; the tree split also keeps
+    // the keys' position ids for its tiles
+    if (tid < D / 2) Rt[tid] = rope_rate(tid, D, log2_base);
+    if (split == S)
+      for (int j = tid; j < n; j += kAttnThreads) Pk[j] = pos[(int64_t)b * N + j];
+    const int qpos = row_ok ? pos[(int64_t)b * N + node] : 0;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float sn, cs;
+        rope_sincos(qpos, Rt[16 * c + 8 * half + e], sn, cs);
+        const float lo = (float)qf[c][e], hi = (float)qf[c + D / 32][e];
+        qf[c][e] = (__bf16)(lo * cs - hi * sn);
+        qf[c + D / 32][e] = (__bf16)(hi * cs + lo * sn);
+      }
+  }
   const uint64_t* arow = anc + ((int64_t)b * N + (row_ok ? node : 0)) * W;
 
   f32x16 oacc[D / 32];
@@ -151,14 +175,29 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
       __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, head_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, head_bytes, 0x00020000);
+  // the thread's KLD 16-byte chunks of a tile: key row and column.  The
+  // rotary tree split takes them in pairs (chunk j, chunk j + KCH/2 of one
+  // row), the two halves of a rotation pair
+  int ckey[KLD], ccol[KLD];
+#pragma unroll
+  for (int i = 0; i < KLD; ++i) {
+    if (ROPE && split == S) {
+      const int pi = tid + (i >> 1) * kAttnThreads;
+      ckey[i] = pi / (KCH / 2);
+      ccol[i] = (pi % (KCH / 2) + (i & 1) * (KCH / 2)) * 8;
+    } else {
+      const int c = tid + i * kAttnThreads;
+      ckey[i] = c / KCH;
+      ccol[i] = (c % KCH) * 8;
+    }
+  }
   uint4 kreg[KLD], vreg[KLD];
   auto fetch = [&](int kt) {
     if (kt + kTileKeys <= k1) {  // whole tile
       const uint32_t soff = (uint32_t)kt * D * 2u;
 #pragma unroll
       for (int i = 0; i < KLD; ++i) {
-        const int c = tid + i * kAttnThreads;
-        const uint32_t voff = (uint32_t)((c / KCH) * D + (c % KCH) * 8) * 2u;
+        const uint32_t voff = (uint32_t)(ckey[i] * D + ccol[i]) * 2u;
         kreg[i] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(
                        krs, voff, soff, 0));
@@ -169,8 +208,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
     } else {
 #pragma unroll
       for (int i = 0; i < KLD; ++i) {
-        const int c = tid + i * kAttnThreads;
-        const uint32_t voff = (uint32_t)(min(kt + c / KCH, k1 - 1) * D + (c % KCH) * 8) * 2u;
+        const uint32_t voff = (uint32_t)(min(kt + ckey[i], k1 - 1) * D + ccol[i]) * 2u;
         kreg[i] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(
                        krs, voff, 0, 0));
@@ -182,10 +220,30 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
   };
   auto stage = [&](int kt) {
     const bool whole = kt + kTileKeys <= k1;
+    if constexpr (ROPE) {
+      if (split == S) {  // tree keys: turn each pair at the key's position id
+#pragma unroll
+        for (int i = 0; i < KLD; i += 2) {
+          const int t = kt - L + ckey[i];
+          const int kp = t < n ? Pk[t] : 0;  // rows past the end stage as zeros
+          bf16x8 lo = __builtin_bit_cast(bf16x8, kreg[i]);
+          bf16x8 hi = __builtin_bit_cast(bf16x8, kreg[i + 1]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float sn, cs;
+            rope_sincos(kp, Rt[ccol[i] + e], sn, cs);
+            const float xl = (float)lo[e], xh = (float)hi[e];
+            lo[e] = (__bf16)(xl * cs - xh * sn);
+            hi[e] = (__bf16)(xh * cs + xl * sn);
+          }
+          kreg[i] = __builtin_bit_cast(uint4, lo);
+          kreg[i + 1] = __builtin_bit_cast(uint4, hi);
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < KLD; ++i) {
-      const int c = tid + i * kAttnThreads;
-      const int key = c / KCH, col = (c % KCH) * 8;
+      const int key = ckey[i], col = ccol[i];
       uint4 kv = kreg[i], vv = vreg[i];
       if (!whole && kt + key >= k1) {  // rows past the end stage as zeros
         kv = make_uint4(0, 0, 0, 0);
@@ -431,6 +489,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(const uint16_t* __restrict
 // ---------------------------------------------------------------------------
 // fp32 path: one workgroup per (sequence, node, head); two passes over keys.
 // ---------------------------------------------------------------------------
+template <bool ROPE>
 __global__ __launch_bounds__(256) void k_attn_f32(const float* __restrict__ q,
                                                  const float* __restrict__ kc,
                                                  const float* __restrict__ vc,
@@ -439,8 +498,11 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float* __restrict__ q,
                                                  const int* __restrict__ n_nodes, int N, int Hq,
                                                  int Hkv, int D, int cap, float scale,
                                                  float* __restrict__ out,
-                                                 float* __restrict__ lse) {
+                                                 float* __restrict__ lse,
+                                                 const int* __restrict__ pos,
+                                                 double log2_base) {
   __shared__ float qs[128];
+  __shared__ double rt[ROPE ? 64 : 1];
   __shared__ float ps[256];
   __shared__ float red[256 / WAVE];
   const int64_t rowid = blockIdx.x;
@@ -461,6 +523,17 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float* __restrict__ q,
   const float* kb = kc + ((int64_t)b * Hkv + g) * (int64_t)cap * D;
   const float* vb = vc + ((int64_t)b * Hkv + g) * (int64_t)cap * D;
   for (int d = tid; d < D; d += 256) qs[d] = q[rowid * D + d];
+  if constexpr (ROPE) {  // the query and the tree keys turn at their position ids
+    if (tid < D / 2) rt[tid] = rope_rate(tid, D, log2_base);
+    __syncthreads();
+    if (tid < D / 2) {
+      float sn, cs;
+      rope_sincos(pos[(int64_t)b * N + node], rt[tid], sn, cs);
+      const float lo = qs[tid], hi = qs[tid + D / 2];
+      qs[tid] = lo * cs - hi * sn;
+      qs[tid + D / 2] = hi * cs + lo * sn;
+    }
+  }
   __syncthreads();
   const int nk = L + n;
   auto visible = [&](int key) {
@@ -471,7 +544,17 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float* __restrict__ q,
   auto score = [&](int key) {
     const float* kr = kb + (int64_t)key * D;
     float a = 0.f;
-    for (int d = 0; d < D; ++d) a += qs[d] * kr[d];
+    if (ROPE && key >= L) {
+      const int kp = pos[(int64_t)b * N + (key - L)];
+      for (int d = 0; d < D / 2; ++d) {
+        float sn, cs;
+        rope_sincos(kp, rt[d], sn, cs);
+        const float lo = kr[d], hi = kr[d + D / 2];
+        a += qs[d] * (lo * cs - hi * sn) + qs[d + D / 2] * (hi * cs + lo * sn);
+      }
+    } else {
+      for (int d = 0; d < D; ++d) a += qs[d] * kr[d];
+    }
     return a * scale;
   };
   float mx = -__builtin_inff();
@@ -539,14 +622,22 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, con
                             bool bf16, const int* ctx_len, const uint64_t* anc,
                             const int* n_nodes, int batch, int N, int Hq, int Hkv, int D,
                             int cap, int max_ctx, float scale, void* out, bool out_f32,
-                            float* lse, void* ws, hipStream_t stream) {
+                            float* lse, const int* pos, double log2_base, void* ws,
+                            hipStream_t stream) {
   (void)max_ctx;
   const int64_t rows = (int64_t)batch * N * Hq;
+  const bool rope = pos != nullptr;
   if (!bf16) {
-    hipLaunchKernelGGL(k_attn_f32, dim3((unsigned)rows), dim3(256), 0, stream,
-                       static_cast<const float*>(q), static_cast<const float*>(k),
-                       static_cast<const float*>(v), ctx_len, anc, n_nodes, N, Hq, Hkv, D, cap,
-                       scale, static_cast<float*>(out), lse);
+#define TV_F32(R)                                                                              \
+  hipLaunchKernelGGL(k_attn_f32<R>, dim3((unsigned)rows), dim3(256), 0, stream,                \
+                     static_cast<const float*>(q), static_cast<const float*>(k),               \
+                     static_cast<const float*>(v), ctx_len, anc, n_nodes, N, Hq, Hkv, D, cap,  \
+                     scale, static_cast<float*>(out), lse, pos, log2_base)
+    if (rope)
+      TV_F32(true);
+    else
+      TV_F32(false);
+#undef TV_F32
     return hipGetLastError();
   }
   char* w = static_cast<char*>(ws);
@@ -560,16 +651,23 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, con
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
-  if (D == 128)
-    hipLaunchKernelGGL((k_attn_partial<128>), dim3(grid), dim3(kAttnThreads), 0, stream, q16,
-                       k16, v16, ctx_len, anc, n_nodes, N, Hq, Hkv, cap, p.splits,
-                       p.keys_per_split, p.mtiles, items, scale_log2, Opart, Mpart, Lpart,
-                       batch);
-  else
-    hipLaunchKernelGGL((k_attn_partial<64>), dim3(grid), dim3(kAttnThreads), 0, stream, q16,
-                       k16, v16, ctx_len, anc, n_nodes, N, Hq, Hkv, cap, p.splits,
-                       p.keys_per_split, p.mtiles, items, scale_log2, Opart, Mpart, Lpart,
-                       batch);
+#define TV_PARTIAL(DD, R)                                                                   \
+  hipLaunchKernelGGL((k_attn_partial<DD, R>), dim3(grid), dim3(kAttnThreads), 0, stream, q16, \
+                     k16, v16, ctx_len, anc, n_nodes, N, Hq, Hkv, cap, p.splits,              \
+                     p.keys_per_split, p.mtiles, items, scale_log2, Opart, Mpart, Lpart, batch, \
+                     pos, log2_base)
+  if (D == 128) {
+    if (rope)
+      TV_PARTIAL(128, true);
+    else
+      TV_PARTIAL(128, false);
+  } else {
+    if (rope)
+      TV_PARTIAL(64, true);
+    else
+      TV_PARTIAL(64, false);
+  }
+#undef TV_PARTIAL
   const unsigned cgrid = (unsigned)((rows + (256 / (D / 4)) - 1) / (256 / (D / 4)));
   if (out_f32)
     hipLaunchKernelGGL((k_attn_combine<float>), dim3(cgrid), dim3(256), 0, stream, Opart, Mpart,

@@ -94,10 +94,41 @@ __device__ __forceinline__ u64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_
 constexpr uint64_t kResidualSlot = 0xFFFFFFFFull;
 
 // ---------------------------------------------------------------------------
+// rotary position embedding: dimension i < D/2 pairs with i + D/2 and the pair
+// turns by the angle pos * base^(-2i/D) (the half-split pairing of the
+// standard rotary embedding)
+// ---------------------------------------------------------------------------
+// pair i's angle per unit of position, in revolutions: base^(-2i/D) / (2 pi)
+__device__ __forceinline__ double rope_rate(int i, int D, double log2_base) {
+  return exp2(-2.0 * (double)i / (double)D * log2_base) * 0.15915494309189535;
+}
+
+// sin and cos of position pos at `rate`: pos * rate in fp64, reduced to
+// [-1/2, 1/2] revolutions, then sin / cos of pi * (2 f) in fp32
+__device__ __forceinline__ void rope_sincos(int pos, double rate, float& s, float& c) {
+  const double r = (double)pos * rate;
+  const float f = (float)(r - rint(r));
+  sincospif(2.0f * f, &s, &c);
+}
+
+// ---------------------------------------------------------------------------
 // element loads
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t h) { return bf16_to_f32(h); }
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) {
+  return x;
+}
+template <>
+__device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) {  // round to nearest even
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
 template <typename T>

@@ -63,7 +63,8 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, con
                             bool bf16, const int* ctx_len, const uint64_t* anc,
                             const int* n_nodes, int batch, int N, int Hq, int Hkv, int D,
                             int cap, int max_ctx, float scale, void* out, bool out_f32,
-                            float* lse, void* ws, hipStream_t stream);
+                            float* lse, const int* pos, double log2_base, void* ws,
+                            hipStream_t stream);
 
 // ---- accept ----
 constexpr int kAcceptChunk = 4096;  // tokens per block in the logits passes
@@ -92,6 +93,6 @@ constexpr int kCommitMaxWidth = 1024;
 hipError_t launch_kv_commit(void* k_cache, void* v_cache, int elem_bytes, int batch, int Hkv,
                             int cap, int D, const int* ctx_len, const int* accept_len,
                             const int* accepted_nodes, int width, int* new_ctx_len,
-                            hipStream_t stream);
+                            bool rope, double log2_base, hipStream_t stream);
 
 }  // namespace tvk
