@@ -202,7 +202,8 @@ tv_status tv_tree_attention_verify(const void *q, const void *k_cache, const voi
  *   pos        int32 [batch][N] position ids (tv_tree_build's pos)
  *   rope_base  finite, > 1 (e.g. 1e4, 1e6); other arguments as above.
  * Rotated bf16 values are rounded to bf16 (nearest even) before the matrix
- * products; angles are reduced in fp64 before fp32 sin/cos.
+ * products; angles are reduced in fp64 to [-1/2, 1/2] revolutions before the
+ * hardware fp32 sine and cosine (abs error below 2e-7).
  * ------------------------------------------------------------------------ */
 tv_status tv_tree_attention_verify_rope(const void *q, const void *k_cache, const void *v_cache,
                                         tv_dtype dt, const int32_t *ctx_len,

@@ -131,26 +131,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
       qf[c] = __builtin_bit_cast(bf16x8, raw);
     }
   }
+  // rotary embedding at the tree position ids (pos[b][i] = L + depth): the
+  // pair rates and, in the tree split, the keys' position ids go to LDS; the
+  // queries are turned once the first tile's loads are in flight
+  int qpos = 0;
   if constexpr (ROPE) {
-    // the rotary embedding at the tree position ids (pos[b][i] = L + depth):
-    // the lane's Q elements d = 16 c + 8 half + e hold both members of each
-    // pair (d, d + D/2), in chunks c and c + D/32; the tree split also keeps
-    // the keys' position ids for its tiles
     if (tid < D / 2) Rt[tid] = rope_rate(tid, D, log2_base);
     if (split == S)
       for (int j = tid; j < n; j += kAttnThreads) Pk[j] = pos[(int64_t)b * N + j];
-    const int qpos = row_ok ? pos[(int64_t)b * N + node] : 0;
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float sn, cs;
-        rope_sincos(qpos, Rt[16 * c + 8 * half + e], sn, cs);
-        const float lo = (float)qf[c][e], hi = (float)qf[c + D / 32][e];
-        qf[c][e] = (__bf16)(lo * cs - hi * sn);
-        qf[c + D / 32][e] = (__bf16)(hi * cs + lo * sn);
-      }
+    qpos = row_ok ? pos[(int64_t)b * N + node] : 0;
   }
   const uint64_t* arow = anc + ((int64_t)b * N + (row_ok ? node : 0)) * W;
 
@@ -268,6 +257,21 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
     for (int j = 0; j < W; ++j) aw[j] = row_ok ? arow[j] : 0ull;
 
   if (k0 < k1) fetch(k0);
+  if constexpr (ROPE) {
+    // the lane's Q elements d = 16 c + 8 half + e hold both members of each
+    // pair (d, d + D/2), in chunks c and c + D/32
+    lds_barrier();  // Rt and Pk written (the tile loads stay in flight)
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float sn, cs;
+        rope_sincos(qpos, Rt[16 * c + 8 * half + e], sn, cs);
+        const float lo = (float)qf[c][e], hi = (float)qf[c + D / 32][e];
+        qf[c][e] = (__bf16)(lo * cs - hi * sn);
+        qf[c + D / 32][e] = (__bf16)(hi * cs + lo * sn);
+      }
+  }
   for (int kt = k0; kt < k1; kt += kTileKeys) {
     stage(kt);
     lds_barrier();
