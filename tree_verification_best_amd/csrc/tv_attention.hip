@@ -36,9 +36,10 @@ namespace tvk {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kTileKeys = 64;  // keys staged per iteration (two 32-key MFMA sub-tiles)
-constexpr int kAttnWaves = 4;  // waves per workgroup, 32 query rows each
-constexpr int kAttnThreads = kAttnWaves * WAVE;
+constexpr int kTileKeys = 64;  // keys one wave takes per iteration (two 32-key MFMA sub-tiles)
+constexpr int kAttnWaves = 4;  // row blocks per workgroup, 32 query rows each
+constexpr int kAttnKH = 2;     // waves per row block: they split each staged tile's keys
+constexpr int kAttnThreads = kAttnWaves * WAVE * kAttnKH;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -68,8 +69,12 @@ __device__ __forceinline__ void lds_barrier() {
 // XCD w % 8), so workgroup w takes item (w % 8) * per + w / 8: every XCD gets
 // a contiguous range of items, i.e. all the splits of a few (KV head, row
 // tile) pairs, and the Q rows and K/V of a head stay in one XCD's L2.
+//
+// Within a workgroup, the kAttnKH waves of one row block take the kAttnKH
+// 64-key quarters of every staged tile (two waves per SIMD), each with its own
+// online softmax; their (m, l, O) are merged through LDS at the end.
 template <int D, bool ROPE>
-__global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
+__global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int* __restrict__ ctx_len,
     const uint64_t* __restrict__ anc, const int* __restrict__ n_nodes, int N, int Hq, int Hkv,
@@ -80,9 +85,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
   constexpr int VP = D + 16;  // V tile pitch (bf16): the 16 rows of a transposing read
                               // (4 keys x 4 column groups) fall in distinct banks
   constexpr int KCH = D / 8;  // 16-byte chunks per key row
-  constexpr int KLD = kTileKeys * KCH / kAttnThreads;  // K (and V) chunks per thread
-  __shared__ __align__(16) uint16_t Ks[kTileKeys * KP];
-  __shared__ __align__(16) uint16_t Vs[kTileKeys * VP];
+  constexpr int TK = kTileKeys * kAttnKH;       // keys staged per iteration
+  constexpr int KLD = TK * KCH / kAttnThreads;  // K (and V) chunks per thread
+  __shared__ __align__(16) uint16_t Ks[TK * KP];
+  __shared__ __align__(16) uint16_t Vs[TK * VP];
   __shared__ uint64_t Aw[kAttnWaves * 32 * 16];  // ancestor rows (tree split)
   __shared__ double Rt[ROPE ? D / 2 : 1];         // rotary rate of each pair
   __shared__ int Pk[ROPE ? 1024 : 1];             // position ids of the tree keys
@@ -104,8 +110,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
   const int tid = threadIdx.x;
   const int wave = tid / WAVE, lane = tid % WAVE;
   const int half = lane >> 5, l32 = lane & 31;
+  const int rb = wave % kAttnWaves, kh = wave / kAttnWaves;  // row block, key quarter
 
-  const int row0 = (mt * kAttnWaves + wave) * 32;
+  const int row0 = (mt * kAttnWaves + rb) * 32;
   const int row = row0 + l32;
   const int node = row / G;
   const int h = g * G + row % G;
@@ -123,13 +130,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
 
   bf16x8 qf[D / 16];
   {
-    const uint16_t* qp = q + (((int64_t)b * N + (row_ok ? node : 0)) * Hq + h) * D;
+    // the address does not depend on n_nodes, so the loads leave before the
+    // scalar loads of the lengths return; rows past n_nodes are masked in
+    // the loop (their scores are replaced, never used)
+    const uint16_t* qp = q + (((int64_t)b * N + min(node, N - 1)) * Hq + h) * D;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      uint4 raw = row_ok ? *reinterpret_cast<const uint4*>(qp + c * 16 + half * 8)
-                         : make_uint4(0, 0, 0, 0);
-      qf[c] = __builtin_bit_cast(bf16x8, raw);
-    }
+    for (int c = 0; c < D / 16; ++c)
+      qf[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + c * 16 + half * 8));
   }
   // rotary embedding at the tree position ids (pos[b][i] = L + depth): the
   // pair rates and, in the tree split, the keys' position ids go to LDS; the
@@ -181,8 +188,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
     }
   }
   uint4 kreg[KLD], vreg[KLD];
+  // the first tile of a context split, before ctx_len is known: rows are
+  // clamped to the head's last cache row (always in bounds); rows past the
+  // split's end are zeroed when staged
+  auto fetch_first = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const uint32_t voff = (uint32_t)(min(kt + ckey[i], cap - 1) * D + ccol[i]) * 2u;
+      kreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff, 0, 0));
+      vreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, 0, 0));
+    }
+  };
   auto fetch = [&](int kt) {
-    if (kt + kTileKeys <= k1) {  // whole tile
+    if (kt + TK <= k1) {  // whole tile
       const uint32_t soff = (uint32_t)kt * D * 2u;
 #pragma unroll
       for (int i = 0; i < KLD; ++i) {
@@ -208,7 +226,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
     }
   };
   auto stage = [&](int kt) {
-    const bool whole = kt + kTileKeys <= k1;
+    const bool whole = kt + TK <= k1;
     if constexpr (ROPE) {
       if (split == S) {  // tree keys: turn each pair at the key's position id
 #pragma unroll
@@ -252,11 +270,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
   // issues no global load other than the K/V prefetch: waiting for any other
   // load would also wait for the prefetch (the vector memory counter retires
   // in order).
-  uint64_t* aw = &Aw[(wave * 32 + l32) * 16];
-  if (split == S && half == 0)
+  uint64_t* aw = &Aw[(rb * 32 + l32) * 16];
+  if (split == S && half == 0 && kh == 0)
     for (int j = 0; j < W; ++j) aw[j] = row_ok ? arow[j] : 0ull;
 
-  if (k0 < k1) fetch(k0);
+  // a context split's first tile starts at split * KS whatever the context
+  // length, so its loads leave without waiting for ctx_len
+  if (split < S)
+    fetch_first(k0);
+  else if (k0 < k1)
+    fetch(k0);
   if constexpr (ROPE) {
     // the lane's Q elements d = 16 c + 8 half + e hold both members of each
     // pair (d, d + D/2), in chunks c and c + D/32
@@ -272,12 +295,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
         qf[c + D / 32][e] = (__bf16)(hi * cs + lo * sn);
       }
   }
-  for (int kt = k0; kt < k1; kt += kTileKeys) {
-    stage(kt);
+  for (int kt0 = k0; kt0 < k1; kt0 += TK) {
+    stage(kt0);
     lds_barrier();
-    if (kt + kTileKeys < k1) fetch(kt + kTileKeys);  // in flight during the products
+    if (kt0 + TK < k1) fetch(kt0 + TK);  // in flight during the products
 
-    if (wave_active) {
+    const int kt = kt0 + kTileKeys * kh;  // this wave's 64 keys: tile rows kr0 ..
+    const int kr0 = kTileKeys * kh;
+    if (wave_active && kt < k1) {
       // visibility of the 64 keys, taken before the matrix products so that
       // their results are consumed in straight-line code.  valid bit j =
       // key kt + j exists for this row; the lane's 32 keys are nibbles
@@ -305,9 +330,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
         const bf16x8 a0 = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4*>(&Ks[l32 * KP + c * 16 + half * 8]));
+            bf16x8, *reinterpret_cast<const uint4*>(&Ks[(kr0 + l32) * KP + c * 16 + half * 8]));
         const bf16x8 a1 = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4*>(&Ks[(32 + l32) * KP + c * 16 + half * 8]));
+            bf16x8,
+            *reinterpret_cast<const uint4*>(&Ks[(kr0 + 32 + l32) * KP + c * 16 + half * 8]));
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[c], s1, 0, 0, 0);
       }
@@ -358,7 +384,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
           bf16x8 bp;
 #pragma unroll
           for (int j = 0; j < 8; ++j) bp[j] = (__bf16)p[16 * ks + 8 * t + j];
-          const int rr = 32 * ks + 16 * t + tr_key;  // key rows rr and rr + 8
+          const int rr = kr0 + 32 * ks + 16 * t + tr_key;  // key rows rr and rr + 8
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
             // A = V^T: d = 32 db + lane % 32; k-slots 0..3 and 4..7 of the lane
@@ -379,6 +405,38 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_partial(
   // loop body, a different basic block: wait out the result latency before
   // the stores read them.
   __builtin_amdgcn_s_sleep(2);
+  // merge the key quarters of each row block: waves kh > 0 hand (O, m, l)
+  // over through LDS (the tiles are free: every wave has passed the loop's
+  // last barrier), stored value-major so that consecutive lanes hit
+  // consecutive banks; wave kh = 0 rescales both to the larger maximum
+  {
+    constexpr int NJ = 16 * (D / 32) + 2;  // floats per lane: O, m, l
+    static_assert(2 * NJ * WAVE * 4 <= TK * KP * 2, "exchange fits the K tile");
+    static_assert(kAttnKH == 2, "one partner wave per row block");
+    float* xo = reinterpret_cast<float*>(rb < 2 ? Ks : Vs) + (rb & 1) * NJ * WAVE;
+    if (kh == 1) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xo[(db * 16 + i) * WAVE + lane] = oacc[db][i];
+      xo[(NJ - 2) * WAVE + lane] = m_run;
+      xo[(NJ - 1) * WAVE + lane] = l_run;
+    }
+    lds_barrier();
+    if (kh != 0) return;  // no barrier follows
+    const float mb = xo[(NJ - 2) * WAVE + lane], lb = xo[(NJ - 1) * WAVE + lane];
+    const float mm = fmaxf(m_run, mb);
+    const float aa =
+        m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m_run - mm) * scale_log2);
+    const float ab = mb == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((mb - mm) * scale_log2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        oacc[db][i] = oacc[db][i] * aa + xo[(db * 16 + i) * WAVE + lane] * ab;
+    l_run = l_run * aa + lb * ab;
+    m_run = mm;
+  }
   const float l_tot = l_run + xor32_f(l_run);
   if (row_ok) {
     const int64_t pr = (((int64_t)split * batch + b) * N + node) * Hq + h;
@@ -598,16 +656,36 @@ AttnPlan attention_plan(int batch, int N, int Hq, int Hkv, int D, int max_ctx, i
   p.waves = kAttnWaves;
   p.mtiles = (p.row_blocks + kAttnWaves - 1) / kAttnWaves;
   const int tiles_ctx = std::max(1, (max_ctx + kTileKeys - 1) / kTileKeys);
+  // whole staged tiles (kAttnKH 64-key quarters) per split
+  auto tiles_per_split = [&](int S) {
+    const int tps = (tiles_ctx + S - 1) / S;
+    return ((tps + kAttnKH - 1) / kAttnKH) * kAttnKH;
+  };
   int S = splits;
   if (S <= 0) {
-    // about four workgroups per CU (two resident), at least 8 key tiles
-    // (512 keys) per split so the partials stay well below the K/V bytes
+    // A cost model fitted to measured times on the 256-CU part: one
+    // workgroup per CU at a time, each paying a fixed ~13 us (launch,
+    // prologue loads, partial stores) plus ~1 us per 64-key tile, in
+    // ceil(workgroups / 256) rounds; then the combine, ~3.5 us plus its
+    // partial reads at ~5 TB/s.  Fewer splits mean longer loops, more
+    // splits more rounds and more partial traffic.
     const int64_t wg_per_split = (int64_t)batch * Hkv * p.mtiles;
-    S = (int)std::max<int64_t>(1, (1024 + wg_per_split - 1) / wg_per_split);
-    S = std::min(S, std::max(1, tiles_ctx / 8));
+    const double part_bytes = (double)batch * N * Hq * (D * 2 + 8);
+    double best = 1e300;
+    for (int c = 1; c <= std::min(tiles_ctx, 64); ++c) {
+      const int tps = tiles_per_split(c);
+      const int sp = (tiles_ctx + tps - 1) / tps;
+      if (sp != c) continue;  // the same as a smaller count
+      const int64_t rounds = (wg_per_split * (sp + 1) + 255) / 256;
+      const double cost = rounds * (13.0 + tps) + 3.5 + part_bytes * (sp + 1) / 5e6;
+      if (cost < best) {
+        best = cost;
+        S = c;
+      }
+    }
   }
   S = std::max(1, std::min(S, tiles_ctx));
-  p.keys_per_split = ((tiles_ctx + S - 1) / S) * kTileKeys;
+  p.keys_per_split = tiles_per_split(S) * kTileKeys;
   p.splits = (tiles_ctx * kTileKeys + p.keys_per_split - 1) / p.keys_per_split;
   const size_t rows = (size_t)(p.splits + 1) * batch * N * Hq;
   size_t off = 0;
