@@ -409,11 +409,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
   // over through LDS (the tiles are free: every wave has passed the loop's
   // last barrier), stored value-major so that consecutive lanes hit
   // consecutive banks; wave kh = 0 rescales both to the larger maximum
+  constexpr int NJ = 16 * (D / 32) + 2;  // floats per lane: O, m, l
+  static_assert(2 * NJ * WAVE * 4 <= TK * KP * 2, "exchange fits the K tile");
+  static_assert(kAttnKH == 2, "one partner wave per row block");
+  float* xo = reinterpret_cast<float*>(rb < 2 ? Ks : Vs) + (rb & 1) * NJ * WAVE;
   {
-    constexpr int NJ = 16 * (D / 32) + 2;  // floats per lane: O, m, l
-    static_assert(2 * NJ * WAVE * 4 <= TK * KP * 2, "exchange fits the K tile");
-    static_assert(kAttnKH == 2, "one partner wave per row block");
-    float* xo = reinterpret_cast<float*>(rb < 2 ? Ks : Vs) + (rb & 1) * NJ * WAVE;
     if (kh == 1) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
@@ -438,20 +438,25 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
     m_run = mm;
   }
   const float l_tot = l_run + xor32_f(l_run);
-  if (row_ok) {
+  if (row_ok && half == 0) {
     const int64_t pr = (((int64_t)split * batch + b) * N + node) * Hq + h;
-    if (half == 0) {
-      Mpart[pr] = m_run * scale_log2;  // log2 domain (-inf stays -inf)
-      Lpart[pr] = l_tot;
-    }
-    // O / l in fp16: a weighted mean of V rows, so it stays within V's range
+    Mpart[pr] = m_run * scale_log2;  // log2 domain (-inf stays -inf)
+    Lpart[pr] = l_tot;
+  }
+  // O / l in fp16 (a weighted mean of V rows, so it stays within V's range).
+  // The accumulator gives a lane 4-column runs of one row; the rows go
+  // through this wave's own exchange region (read above, used by no other
+  // wave) so that every store is a whole 16-byte chunk and each store
+  // instruction covers 1 KB of consecutive partial rows.
+  {
+    constexpr int OP = D + 8;  // LDS row pitch (fp16)
+    static_assert(32 * OP * 2 <= NJ * WAVE * 4, "rows fit the exchange region");
+    uint16_t* tw = reinterpret_cast<uint16_t*>(xo);
     const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* op = Opart + pr * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int d0 = 32 * db + 8 * j + 4 * half;
         uint32_t w2[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -460,8 +465,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
           w2[t] = (uint32_t)__builtin_bit_cast(uint16_t, x0) |
                   ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
         }
-        *reinterpret_cast<uint2*>(op + d0) = make_uint2(w2[0], w2[1]);
+        *reinterpret_cast<uint2*>(&tw[l32 * OP + 32 * db + 8 * j + 4 * half]) =
+            make_uint2(w2[0], w2[1]);
       }
+    constexpr int CPR = D / 8;  // 16-byte chunks per row
+#pragma unroll
+    for (int k = 0; k < 32 * CPR / WAVE; ++k) {
+      const int ch = k * WAVE + lane, r = ch / CPR, c16 = ch % CPR;
+      const uint4 x = *reinterpret_cast<const uint4*>(&tw[r * OP + c16 * 8]);
+      const int rowg = row0 + r, nd = rowg / G;
+      if (nd < n) {
+        const int64_t pr = (((int64_t)split * batch + b) * N + nd) * Hq + g * G + rowg % G;
+        *reinterpret_cast<uint4*>(Opart + pr * D + c16 * 8) = x;
+      }
+    }
   }
 }
 
