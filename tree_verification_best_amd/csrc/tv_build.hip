@@ -568,50 +568,64 @@ __global__ __launch_bounds__(WAVE) void k_tree_budget(const double* __restrict__
                                                      const int* __restrict__ n_nodes,
                                                      const double* __restrict__ cost, int N,
                                                      int* n_out) {
+  constexpr int NC = 16;  // 64-row chunks of a tree of up to 1024 rows
   __shared__ double S[1024];
   const int b = blockIdx.x, lane = lane_id();
-  // the first 64 scores (every row below N exists) travel with n_nodes
-  const double x0 = 1 + lane < N ? score[(int64_t)b * N + 1 + lane] : 0.0;
+  // every load leaves at once: the scores and costs of rows below N exist
+  // whatever n_nodes says (chunk k holds scores 1 + 64 k + lane, costs
+  // 64 k + lane)
+  double x[NC], c[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int i = 1 + 64 * k + lane, m = 64 * k + lane;
+    x[k] = i < N ? score[(int64_t)b * N + i] : 0.0;
+    c[k] = m < N ? cost[m] : 1.0;
+  }
   const int n = n_nodes[b];
   if (n < 1 || n > N) {
     if (lane == 0) n_out[b] = n;
     return;
   }
+  // S_i = S_{i-1} + s_i in order: a uniform chain over the lanes' scores
   double run = 0.0;
   if (lane == 0) S[0] = 0.0;
-  for (int i0 = 1; i0 < n; i0 += WAVE) {
-    const double x = i0 == 1 ? x0 : (i0 + lane < n ? score[(int64_t)b * N + i0 + lane] : 0.0);
-    const int m = min(WAVE, n - i0);
-    double mine = 0.0;
-    for (int j = 0; j < m; ++j) {
-      run = run + readlane_d(x, j);
-      if (lane == j) mine = run;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int i0 = 1 + 64 * k;
+    if (i0 < n) {
+      const int m = min(WAVE, n - i0);
+      double mine = 0.0;
+      for (int j = 0; j < m; ++j) {
+        run = run + readlane_d(x[k], j);
+        if (lane == j) mine = run;
+      }
+      if (lane < m) S[i0 + lane] = mine;
     }
-    if (lane < m) S[i0 + lane] = mine;
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // each lane rates its sizes m = 64 k + lane (ascending, so a strict
+  // improvement keeps the smallest size on ties), then the wave takes the
+  // largest ratio and, among equal ratios, the smallest size.  Ratios are
+  // positive, so their bit patterns order as the values do.
   double best_r = -1.0;
   int best_n = 0x7fffffff;
-  for (int m = lane; m < n; m += WAVE) {
-    const double r = (1.0 + S[m]) / cost[m];
-    if (r > best_r) {  // ascending m: the smallest size wins a tie
-      best_r = r;
-      best_n = m;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int m = 64 * k + lane;
+    if (m < n) {
+      const double r = (1.0 + S[m]) / c[k];
+      if (r > best_r) {
+        best_r = r;
+        best_n = m;
+      }
     }
   }
-  double br = readlane_d(best_r, 0);
-  int bn = readlane_i(best_n, 0);
-  for (int j = 1; j < WAVE; ++j) {
-    const double r = readlane_d(best_r, j);
-    const int m = readlane_i(best_n, j);
-    if (r > br || (r == br && m < bn)) {
-      br = r;
-      bn = m;
-    }
-  }
-  if (lane == 0) n_out[b] = bn + 1;
+  const uint64_t key = best_r > 0.0 ? __builtin_bit_cast(uint64_t, best_r) : 0ull;
+  const uint64_t top = ~wave_min_u64(~key);
+  const uint64_t bn = wave_min_u64(key == top ? (uint64_t)best_n : ~0ull);
+  if (lane == 0) n_out[b] = (int)bn + 1;
 }
 
 // A tree of capacity N holding only its root (row 0), in the row layout of
