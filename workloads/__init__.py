@@ -58,12 +58,11 @@ STREAM_DRAFT, STREAM_TARGET, STREAM_Q, STREAM_K, STREAM_V, STREAM_TREE, STREAM_C
 
 
 def round_bf16(x):
-    """Round float32 values to the nearest bf16 (ties to even); returns float32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    u = (u + 0x7FFF + lsb) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    """Round float32 values to the nearest bf16 (ties to even); returns float32
+    (torch's CPU conversion, multi-threaded, for the large caches)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
 
 
 def logits(cfg, batch, N, salt=0):
