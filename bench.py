@@ -2,6 +2,11 @@
 
 A step is the whole round on one batch of synthetic input already resident in
 HBM: tv_tree_build -> tv_tree_attention_verify (one layer) -> tv_tree_accept.
+The timed steps replay the round captured in a HIP graph (one graph per input
+set; --eager times eager launches instead); the same steps are then run
+eagerly with HIP events around every call, which gives the per-call times and
+the roofline (torch on this platform cannot record timing events inside a
+graph).
 The KV commit that closes a round (tv_kv_commit), the cost-aware tree size
 (tv_tree_budget) and a layer-wise build of the same capacity (tv_tree_root +
 K drafting steps of tv_tree_expand, frontier width 8) are timed after the
@@ -24,7 +29,7 @@ profiles/attention_<workload>_traffic.md when that record was taken on the
 current attention source (else null).  `cpu_baseline` times the CPU oracle
 on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 500] [--warmup 50] [--workload 4b]
+    python bench.py [--gpus 1] [--steps 500] [--warmup 50] [--workload 4b] [--eager]
     python bench.py --copy-calibration      # a plain device copy of known size,
                                             # the reference for the byte counters
 """
@@ -52,7 +57,8 @@ def parse():
     ap.add_argument("--workload", default="4b", choices=["4b", "8b", "long", "batched", "tiny"])
     ap.add_argument("--temperature", type=float, default=1.0, help="0 = greedy")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
-    ap.add_argument("--graph", action="store_true", help="replay each round from a HIP graph")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of replays of captured rounds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -270,54 +276,56 @@ def main():
         tv.tv_kv_commit(s["k"], s["v"], s["ctx"], acc["accept_len"], acc["accepted_nodes"],
                         new_ctx_len=new_ctx)
 
-    graphs = None
-    if args.graph:
-        # one graph per input set; replays alternate sets like the eager loop
+    def eager_steps(first, n, evs=None):
+        for i in range(n):
+            round_(first + i, evs[i] if evs is not None else None)
+
+    for i in range(args.warmup):
+        round_(i)
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    graph_ms = None
+    wall = 0.0
+    if not args.eager:
+        # the timed region: replays of the round captured once per input set
+        # (launches only; the calls allocate nothing and set no memory)
         graphs = []
-        for i in range(nsets):
-            round_(i)
-        torch.cuda.synchronize()
         for i in range(nsets):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 round_(i)
             graphs.append(g)
-        torch.cuda.synchronize()
-
-    def step_fn(i, ev=None):
-        if graphs is not None:
-            if ev is not None:
-                ev[0].record(stream)
+        for i in range(min(args.warmup, 2 * nsets)):
             graphs[i % nsets].replay()
-            if ev is not None:
-                for e in ev[1:]:
-                    e.record(stream)
-        else:
-            round_(i, ev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        for i in range(args.steps):
+            graphs[i % nsets].replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall += time.perf_counter() - t0
+        graph_ms = start.elapsed_time(end) / args.steps
 
-    for i in range(args.warmup):
-        step_fn(i)
-    torch.cuda.synchronize()
-
-    # per-call events on the stream the calls run on
+    # eager launches of the same steps with HIP events around every call on
+    # the stream the calls run on (events cannot be recorded inside a graph
+    # on this platform): the per-call times and the roofline come from here
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for i in range(args.steps):
-        step_fn(args.warmup + i, evs[i] if graphs is None else None)
+    eager_steps(args.warmup, args.steps, evs)
     end.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
+    wall += time.perf_counter() - t0
+    eager_ms = start.elapsed_time(end) / args.steps
+    ms_per_step = graph_ms if graph_ms is not None else eager_ms
 
     calls = {}
-    if graphs is None:
-        for name, (a, z) in (("build", (0, 1)), ("attention", (1, 2)), ("accept", (2, 3))):
-            calls[name] = sum(evs[i][a].elapsed_time(evs[i][z]) for i in range(args.steps)) / args.steps
+    for name, (a, z) in (("build", (0, 1)), ("attention", (1, 2)), ("accept", (2, 3))):
+        calls[name] = sum(evs[i][a].elapsed_time(evs[i][z]) for i in range(args.steps)) / args.steps
     # verification with the rotary embedding fused (queries and tree keys
     # turned at the tree's position ids), per call with events like the plain
     # call, over the same input sets and the last step's tree
@@ -482,8 +490,10 @@ def main():
                                f"{c['dtype']}, batch {b}, ctx {c['L']}, K={K}, top-{c['k']}, "
                                f"B={c['B']}, V={V}, T={args.temperature}",
                    "rounds_per_s": round(rounds_per_s, 2), "nodes": N,
-                   "input_sets": nsets, "graph": bool(args.graph),
-                   "round_algorithmic_MB": round(sum(abytes.values()) / 1e6, 2),
+                   "input_sets": nsets, "graph": not args.eager,
+                   "eager_ms_per_step": round(eager_ms, 5),
+                   "round_algorithmic_MB": round(sum(abytes[n] for n in ("build", "attention", "accept")
+                                                     if n in abytes) / 1e6, 2),
                    "attention_GFLOP": round(aflops / 1e9, 3),
                    "mean_accept_len": float(acc["accept_len"].float().mean().item()),
                    "per_call": per_call, "wall_s": round(wall, 3)},
