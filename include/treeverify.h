@@ -367,8 +367,8 @@ tv_status tv_tree_budget(const double *score, const int32_t *n_nodes, const doub
  *   new_ctx_len             int32 [batch], may be the ctx_len array itself
  * Per sequence: accept_len < 0 (a refused tree) commits nothing and gives
  * new_ctx_len = L_b; a path that does not start at node 0, does not increase
- * strictly, or reaches row cap or beyond is left uncommitted with
- * new_ctx_len = -1.
+ * strictly, does not fit in width, or reaches row cap or beyond (or L_b < 0)
+ * is left uncommitted with new_ctx_len = -1.
  * Limits: D in {64, 128}; width <= 1024.
  * ------------------------------------------------------------------------ */
 tv_status tv_kv_commit(void *k_cache, void *v_cache, tv_dtype dt, int batch, int Hkv, int cap,

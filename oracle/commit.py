@@ -10,7 +10,8 @@ L_b + accept_len[b] + 1.  Rows past it are free for the next round.
 
 A sequence with accept_len[b] < 0 (a walk that refused the tree) is left as
 is, new length L_b.  A path that does not start at node 0, is not strictly
-increasing, or reaches past the cache is left as is, new length -1.
+increasing, does not fit in the width, or reaches past the cache (or a
+negative L_b) is left as is, new length -1.
 
 Layouts: k, v [b][Hkv][cap][D]; ctx_len, accept_len [b];
 accepted_nodes [b][width].
@@ -20,7 +21,7 @@ import numpy as np
 
 def valid_path(path, L, cap):
     return (len(path) >= 1 and path[0] == 0 and all(path[j] < path[j + 1]
-            for j in range(len(path) - 1)) and L + path[-1] < cap)
+            for j in range(len(path) - 1)) and L >= 0 and L + path[-1] < cap)
 
 
 def kv_commit(k, v, ctx_len, accept_len, accepted_nodes):

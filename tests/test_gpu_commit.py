@@ -25,6 +25,9 @@ def _paths(r, b, width, cap, ctx):
         alen[s] = a
     alen[0] = 0                              # the root alone
     alen[1] = -1                             # a refused tree
+    if b > 5:
+        alen[4] = width                      # one past the width
+        alen[5] = 2**31 - 1                  # any value: no overflow
     if b > 3:
         acc[2, 1:3] = [5, 5]                 # not strictly increasing
         alen[2] = max(alen[2], 2)
@@ -39,6 +42,7 @@ def test_commit_matches_oracle(dtype, D):
     r = np.random.default_rng(D + (1 if dtype == "bf16" else 0))
     b, Hkv, cap, width = 7, 3, 160, 40
     ctx = r.integers(0, 100, size=b).astype(np.int32)
+    ctx[6] = -4                              # a negative context length
     k = r.standard_normal((b, Hkv, cap, D)).astype(np.float32)
     v = r.standard_normal((b, Hkv, cap, D)).astype(np.float32)
     if dtype == "bf16":

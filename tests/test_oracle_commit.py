@@ -90,3 +90,19 @@ def test_special_cases():
     # a walk that refused its tree (accept_len -1) commits nothing
     _, _, new = oracle.kv_commit(k, v, np.full(b, L), np.full(b, -1), acc)
     np.testing.assert_array_equal(new, np.full(b, L))
+
+
+def test_out_of_range_lengths_commit_nothing():
+    """accept_len past the width (also INT32_MAX) and a negative context
+    length: nothing moves, new length -1."""
+    r = np.random.default_rng(10)
+    b, Hkv, cap, D = 3, 2, 30, 8
+    k = r.standard_normal((b, Hkv, cap, D)).astype(np.float32)
+    v = r.standard_normal((b, Hkv, cap, D)).astype(np.float32)
+    acc = np.tile(np.arange(6, dtype=np.int32), (b, 1))
+    alen = np.array([6, 2**31 - 1, 3], np.int32)
+    ctx = np.array([4, 4, -3], np.int32)
+    k2, v2, new = oracle.kv_commit(k, v, ctx, alen, acc)
+    np.testing.assert_array_equal(new, [-1, -1, -1])
+    np.testing.assert_array_equal(k2, k)
+    np.testing.assert_array_equal(v2, v)

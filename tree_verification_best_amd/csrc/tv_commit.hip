@@ -29,7 +29,8 @@ constexpr int kCommitBatch = 8;
 constexpr int kCommitMaxPath = 1024;
 
 // Loads sequence b's path into LDS and checks it: it starts at the root,
-// increases strictly and stays inside the cache.  Writes new_ctx_len[b] and
+// increases strictly and stays inside the cache (a negative context length
+// fails the check).  Writes new_ctx_len[b] and
 // returns whether the rows are to be moved.
 __device__ bool commit_path(int b, int cap, const int* ctx_len, const int* accept_len,
                             const int* accepted_nodes, int width, int* new_ctx_len, int* path,
@@ -37,13 +38,14 @@ __device__ bool commit_path(int b, int cap, const int* ctx_len, const int* accep
   const int tid = threadIdx.x;
   L = ctx_len[b];
   a = accept_len[b];
-  const int np = min(a + 1, width);
+  // (no a + 1: accept_len may hold any value)
+  const int np = a < 0 ? 0 : (a < width ? a + 1 : width);
   for (int j = tid; j < np; j += kCommitNT) path[j] = accepted_nodes[(int64_t)b * width + j];
   __syncthreads();
-  int bad = a + 1 > width ? 1 : 0;
+  int bad = a >= width ? 1 : 0;
   for (int j = tid; j < np; j += kCommitNT)
     bad |= j == 0 ? (path[0] != 0) : (path[j] <= path[j - 1]);
-  if (np > 0 && tid == 0) bad |= (int64_t)L + path[np - 1] >= cap ? 1 : 0;
+  if (np > 0 && tid == 0) bad |= (L < 0 || (int64_t)L + path[np - 1] >= cap) ? 1 : 0;
   bad = __syncthreads_or(bad);
   if (tid == 0) new_ctx_len[b] = a < 0 ? L : (bad ? -1 : L + a + 1);
   return a >= 0 && !bad;
