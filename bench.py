@@ -14,6 +14,10 @@ steps, as replays of captured graphs, and reported as per_call.commit,
 per_call.budget and per_call.expand (one drafting step).  The verification
 with the rotary embedding fused (tv_tree_attention_verify_rope, base 1e6) is
 timed per call after the steps and reported as per_call.attention_rope.
+config.b_sweep_ms is the verification time against the tree budget B (one
+sequence, context 4096, B = 16 .. 512), the measured cost that the timed
+tv_tree_budget call takes as its cost curve.  config.cpu_all_cores repeats
+the CPU baseline with the BLAS pool on every usable host core (at most 16).
 The default workload is the 4B-class GQA layer (32 query / 8 KV heads, head
 dim 128, bf16, context 4096, K = 16 draft positions, top-8, budget 64,
 vocabulary 151936, sampled acceptance at T = 1).  Inputs rotate over enough
@@ -129,9 +133,20 @@ def attention_flops(c, n_nodes, depths, ctx):
     return 4 * c["Hq"] * c["D"] * tot
 
 
-def cpu_baseline(c, sets0, seconds):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def cpu_baseline(c, sets0, seconds, threads=1):
     """The oracle, untuned, on the same first input set: whole rounds until
-    `seconds` of CPU time are spent (at least one)."""
+    `seconds` of CPU time are spent (at least one), BLAS limited to
+    `threads`."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -141,7 +156,7 @@ def cpu_baseline(c, sets0, seconds):
     b, N = target.shape[0], target.shape[1]
     mode = oracle.GREEDY if c["_T"] == 0 else oracle.SAMPLED
     rounds, t0 = 0, time.perf_counter()
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         while True:
             if c["build"]:
                 tr = oracle.tree_build(draft, c["k"], c["B"], roots, ctx)
@@ -159,6 +174,48 @@ def cpu_baseline(c, sets0, seconds):
                 break
     dt = time.perf_counter() - t0
     return rounds, dt
+
+
+def b_sweep(c, dev, stream, budgets=(16, 64, 128, 256, 512), L=4096, reps=50):
+    """Verification time (ms per call) of one sequence at context L for each
+    tree budget B, on seeded random trees and Q/K/V."""
+    import numpy as np
+    import torch
+
+    import tree_verification_best_amd as tv
+    import workloads
+
+    nmax = max(budgets) + 1
+    cap = L + nmax
+    q, k, v = workloads.qkv(c, 1, nmax, cap, salt=99)
+    tdt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
+    qd, kd, vd = (torch.from_numpy(a).to(dev, tdt) for a in (q, k, v))
+    ctx = torch.tensor([L], dtype=torch.int32, device=dev)
+    out = {}
+    for B in budgets:
+        N = B + 1
+        parent, _, _ = workloads.random_trees(dict(c, name="sweep"), 1, N, salt=B,
+                                              max_depth=16, max_children=8)
+        nn = torch.tensor([N], dtype=torch.int32, device=dev)
+        t = tv.tv_tree_ancestors(torch.from_numpy(parent).to(dev), nn, ctx)
+        qn = qd[:, :N].contiguous()
+        ws = torch.empty(tv.attention_workspace(1, N, c["Hq"], c["Hkv"], c["D"], L),
+                         dtype=torch.uint8, device=dev)
+        o = torch.empty(qn.shape, dtype=tdt, device=dev)
+        for _ in range(5):
+            tv.tv_tree_attention_verify(qn, kd, vd, ctx, t["anc"], nn, L, workspace=ws, out=o,
+                                        want_lse=False)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            tv.tv_tree_attention_verify(qn, kd, vd, ctx, t["anc"], nn, L, workspace=ws, out=o,
+                                        want_lse=False)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[B] = e0.elapsed_time(e1) / reps
+    return out
 
 
 def main():
@@ -361,10 +418,18 @@ def main():
     c1.record(stream)
     torch.cuda.synchronize()
     calls["commit"] = c0.elapsed_time(c1) / (reps * ncommit)
+    # verification time against the tree budget (the pages' time-vs-budget
+    # figure): one sequence with this workload's heads, context 4096, random
+    # trees of B + 1 nodes, per call with events
+    sweep = b_sweep(c, dev, stream)
     if c["build"]:
-        # the cost-aware tree size over the last step's tree, with an affine
-        # cost per draft node standing in for a measured attention-time sweep
-        cost = torch.tensor([1.0 + 0.01 * i for i in range(N)], dtype=torch.float64, device=dev)
+        # the cost-aware tree size over the last step's tree; the cost of n
+        # draft nodes is the measured verification time, interpolated
+        # between the sweep's budgets
+        import numpy as np
+        sb = sorted(sweep)
+        cost_h = np.interp(np.arange(N), sb, [sweep[x] for x in sb])
+        cost = torch.from_numpy(cost_h).to(dev)
         n_out = torch.empty((b,), **i32)
         bg = torch.cuda.CUDAGraph()
         with torch.cuda.graph(bg):
@@ -465,13 +530,22 @@ def main():
                      "algorithmic_bytes": abytes["attention"], "algorithmic_flops": aflops,
                      "intensity_flop_per_byte": round(intensity, 1)})
 
-    cpu = None
+    cpu = cpu_all = None
     if not args.no_cpu_baseline:
-        r, dt = cpu_baseline(c, first, args.cpu_seconds)
+        model = cpu_model()
+        r, dt = cpu_baseline(c, first, args.cpu_seconds, threads=1)
         cpu = {"value": round(r / dt * rows, 1), "unit": "node-heads/s", "cores": 1,
                "kind": "oracle",
                "sample": f"{r} whole round(s) of the {args.workload} workload (input set 0), "
-                         f"{dt:.1f} s, single thread (BLAS limited to 1)"}
+                         f"{dt:.1f} s, single thread (BLAS limited to 1), {model}"}
+        # the same with the BLAS pool on every host core this process may use
+        # (at most 16, the host share of one GPU); the oracle's C parts stay
+        # single-threaded
+        ncores = min(16, len(os.sched_getaffinity(0)))
+        r, dt = cpu_baseline(c, first, args.cpu_seconds, threads=ncores)
+        cpu_all = {"value": round(r / dt * rows, 1), "unit": "node-heads/s", "cores": ncores,
+                   "kind": "oracle",
+                   "sample": f"{r} whole round(s), {dt:.1f} s, BLAS on {ncores} threads"}
 
     res = {
         "metric": "verify rounds/s as tree node x query-head rows verified per second",
@@ -496,7 +570,9 @@ def main():
                                                      if n in abytes) / 1e6, 2),
                    "attention_GFLOP": round(aflops / 1e9, 3),
                    "mean_accept_len": float(acc["accept_len"].float().mean().item()),
-                   "per_call": per_call, "wall_s": round(wall, 3)},
+                   "per_call": per_call, "wall_s": round(wall, 3),
+                   "b_sweep_ms": {str(k): round(v, 5) for k, v in sweep.items()},
+                   "cpu_all_cores": cpu_all},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
