@@ -7,7 +7,8 @@
  *   tv_tree_attention_verify tree-masked attention of the target over
  *                            context + tree (one layer)
  *   tv_tree_accept           acceptance walk -> accepted path + one token
- * plus tv_tree_ancestors for trees that come from elsewhere, tv_tree_root and
+ * plus tv_tree_ancestors and tv_tree_check for trees that come from
+ * elsewhere, tv_tree_root and
  * tv_tree_expand (a layer-wise builder: root, then one call per drafting
  * step), tv_tree_budget (cost-aware tree size), tv_kv_commit (keep the
  * accepted path in the KV cache) and the rotary-embedding variants
@@ -140,6 +141,26 @@ tv_status tv_tree_build(const void *draft_logits, tv_dtype dt, int batch, int K,
 tv_status tv_tree_ancestors(const int32_t *parent, const int32_t *n_nodes,
                             const int32_t *ctx_len, int batch, int N, int32_t *depth,
                             int32_t *pos, uint64_t *anc_mask, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * tv_tree_check -- structural check of caller-supplied trees.
+ *
+ * The tree arrays of the other calls are preconditions (PTD sec. 3.1: every
+ * node but the root has exactly one parent, so pi(v) = {v} U pi(P(v)) is
+ * well defined; rows are stored parents first).  This call tests them on the
+ * device, without synchronising, so that a caller can check trees from
+ * elsewhere before verification:
+ *   status[b] = 0  the tree is well formed;
+ *             = 1  n_nodes[b] outside [1, N];
+ *             = 2 + i  for the first row i that breaks a rule:
+ *               parent[0] = -1, 0 <= parent[i] < i for 1 <= i < n_nodes[b],
+ *               and, when depth is not NULL, depth[0] = 0 and
+ *               depth[i] = depth[parent[i]] + 1.
+ *   parent, depth int32 [batch][N] (depth may be NULL); n_nodes int32 [batch];
+ *   status int32 [batch] (device).
+ * ------------------------------------------------------------------------ */
+tv_status tv_tree_check(const int32_t *parent, const int32_t *depth, const int32_t *n_nodes,
+                        int batch, int N, int32_t *status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * tv_tree_attention_verify -- one target attention layer over context +

@@ -231,3 +231,27 @@ from .budget import tree_budget  # noqa: E402,F401
 from .expand import tree_expand, tree_root  # noqa: E402,F401
 from .rope import (inv_freq, kv_commit_rope, rope, tree_attention_rope,  # noqa: E402,F401
                    tree_attention_rope_rows)
+
+
+def tree_check(parent, n_nodes, depth=None):
+    """Structural check of trees (PTD sec. 3.1: one parent per node, parents
+    first): 0 well formed, 1 n_nodes outside [1, N], else 2 + the first row
+    breaking parent[0] = -1, 0 <= parent[i] < i, depth[0] = 0 and
+    depth[i] = depth[parent[i]] + 1 (depth when given)."""
+    parent = np.asarray(parent)
+    b, N = parent.shape
+    out = np.zeros(b, np.int32)
+    for s in range(b):
+        n = int(n_nodes[s])
+        if n < 1 or n > N:
+            out[s] = 1
+            continue
+        for i in range(n):
+            p = int(parent[s, i])
+            ok = p == -1 if i == 0 else 0 <= p < i
+            if ok and depth is not None:
+                ok = int(depth[s, 0]) == 0 if i == 0 else int(depth[s, i]) == int(depth[s, p]) + 1
+            if not ok:
+                out[s] = 2 + i
+                break
+    return out

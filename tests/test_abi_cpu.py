@@ -20,7 +20,7 @@ def _declared():
 
 def test_header_functions_exported():
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 17
     lib = ctypes.CDLL(tv.LIBPATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -265,3 +265,11 @@ def test_commit_rope_rejects():
     assert call(base=float("nan")) == tv.TV_ERR_INVALID
     assert call(k=None) == tv.TV_ERR_INVALID
     assert call(D=96) == tv.TV_ERR_UNSUPPORTED
+
+
+def test_check_rejects():
+    L = tv.lib()
+    assert L.tv_tree_check(None, None, FAKE, 1, 8, FAKE, None) == tv.TV_ERR_INVALID
+    assert L.tv_tree_check(FAKE, None, FAKE, 0, 8, FAKE, None) == tv.TV_ERR_INVALID
+    assert L.tv_tree_check(FAKE, None, FAKE, 1, 0, FAKE, None) == tv.TV_ERR_INVALID
+    assert L.tv_tree_check(FAKE, None, FAKE, 1, 8, None, None) == tv.TV_ERR_INVALID

@@ -10,6 +10,7 @@ raise.
 
     tv_tree_build            draft marginals -> prefix-closed draft tree
     tv_tree_ancestors        depth / positions / ancestor rows of a parent array
+    tv_tree_check            structural check of a caller-supplied tree
     tv_tree_attention_verify tree-masked GQA attention over context + tree
     tv_tree_accept           greedy or sampled acceptance walk
     tv_tree_root             a root-only tree (start of a layer-wise build)
@@ -38,7 +39,7 @@ EXPORTS = ("tv_status_string", "tv_version", "tv_tree_build_workspace", "tv_tree
            "tv_tree_ancestors", "tv_tree_attention_workspace", "tv_tree_attention_verify",
            "tv_tree_accept_workspace", "tv_tree_accept", "tv_tree_budget", "tv_kv_commit",
            "tv_tree_root", "tv_tree_expand_workspace", "tv_tree_expand",
-           "tv_tree_attention_verify_rope", "tv_kv_commit_rope")
+           "tv_tree_attention_verify_rope", "tv_kv_commit_rope", "tv_tree_check")
 
 _lib = None
 
@@ -92,6 +93,8 @@ def _load():
     L.tv_kv_commit_rope.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, i32, c.c_double,
                                     vp, vp]
     L.tv_kv_commit_rope.restype = i32
+    L.tv_tree_check.argtypes = [vp, vp, vp, i32, i32, vp, vp]
+    L.tv_tree_check.restype = i32
     L.tv_tree_root.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     L.tv_tree_root.restype = i32
     L.tv_tree_expand_workspace.argtypes = [i32, i32, i32, i32]
@@ -316,6 +319,21 @@ def tv_tree_budget(score, n_nodes, cost, n_nodes_out=None):
                           _dev(n_nodes_out, "n_nodes_out", torch.int32), _stream(score.device))
     _check(st, "tv_tree_budget")
     return n_nodes_out
+
+
+def tv_tree_check(parent, n_nodes, depth=None, status=None):
+    """parent [b][N] (and optionally depth) -> status [b] int32: 0 well formed,
+    1 n_nodes outside [1, N], 2 + i for the first row i that breaks a rule."""
+    L = _load()
+    b, N = parent.shape
+    if status is None:
+        status = torch.empty((b,), dtype=torch.int32, device=parent.device)
+    st = L.tv_tree_check(_dev(parent, "parent", torch.int32),
+                         _dev(depth, "depth", torch.int32) if depth is not None else None,
+                         _dev(n_nodes, "n_nodes", torch.int32), b, N,
+                         _dev(status, "status", torch.int32), _stream(parent.device))
+    _check(st, "tv_tree_check")
+    return status
 
 
 def tree_expand_workspace(batch, W, V, m):

@@ -83,6 +83,13 @@ tv_status tv_tree_build(const void* draft_logits, tv_dtype dt, int batch, int K,
                                          stream));
 }
 
+tv_status tv_tree_check(const int32_t* parent, const int32_t* depth, const int32_t* n_nodes,
+                        int batch, int N, int32_t* status, hipStream_t stream) {
+  if (!parent || !n_nodes || !status) return TV_ERR_INVALID;
+  if (batch < 1 || N < 1) return TV_ERR_INVALID;
+  return device_status(tvk::launch_tree_check(parent, depth, n_nodes, batch, N, status, stream));
+}
+
 tv_status tv_tree_root(const int32_t* root_token, const int32_t* ctx_len, int batch, int N,
                        int32_t* parent, int32_t* token, int32_t* depth, int32_t* pos,
                        double* score, uint64_t* anc_mask, int32_t* n_nodes, hipStream_t stream) {

@@ -839,6 +839,49 @@ hipError_t launch_tree_expand(const BuildPlan& p, const void* logits, bool bf16,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Structural check of caller-supplied trees (PTD sec. 3.1: every node but the
+// root has one parent, and a node's ancestors precede it).  status[b] = 0 for
+// a well-formed tree, 1 for n_nodes outside [1, N], else 2 + the first row
+// that breaks a rule: parent[0] = -1, 0 <= parent[i] < i for 1 <= i < n,
+// and, when depth is given, depth[0] = 0 and depth[i] = depth[parent[i]] + 1.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBuildNT) void k_tree_check(const int* __restrict__ parent,
+                                                        const int* __restrict__ depth,
+                                                        const int* __restrict__ n_nodes, int N,
+                                                        int* __restrict__ status) {
+  __shared__ uint64_t wmin[kBuildNT / WAVE];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int n = n_nodes[b];
+  if (n < 1 || n > N) {
+    if (tid == 0) status[b] = 1;
+    return;
+  }
+  const int64_t rb = (int64_t)b * N;
+  int first = 0x7fffffff;
+  for (int i = tid; i < n && first == 0x7fffffff; i += kBuildNT) {
+    const int p = parent[rb + i];
+    bool ok = i == 0 ? p == -1 : (p >= 0 && p < i);
+    if (ok && depth) ok = i == 0 ? depth[rb] == 0 : depth[rb + i] == depth[rb + p] + 1;
+    if (!ok) first = i;
+  }
+  const uint64_t m = wave_min_u64((uint64_t)(uint32_t)first);
+  if (lane_id() == 0) wmin[tid / WAVE] = m;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t f = wmin[0];
+    for (int w = 1; w < kBuildNT / WAVE; ++w) f = umin64(f, wmin[w]);
+    status[b] = f == 0x7fffffffull ? 0 : 2 + (int)f;
+  }
+}
+
+hipError_t launch_tree_check(const int* parent, const int* depth, const int* n_nodes, int batch,
+                             int N, int* status, hipStream_t stream) {
+  hipLaunchKernelGGL(k_tree_check, dim3(batch), dim3(kBuildNT), 0, stream, parent, depth,
+                     n_nodes, N, status);
+  return hipGetLastError();
+}
+
 hipError_t launch_tree_root(const int* root_token, const int* ctx_len, int batch, int N,
                             int* parent, int* token, int* depth, int* pos, double* score,
                             uint64_t* anc, int* n_nodes, hipStream_t stream) {

@@ -37,6 +37,8 @@ hipError_t launch_tree_expand(const BuildPlan& p, const void* logits, bool bf16,
                               const int* frontier, int* parent, int* token, int* depth, int* pos,
                               double* score, uint64_t* anc, int* n_nodes, int* next_frontier,
                               void* ws, hipStream_t stream);
+hipError_t launch_tree_check(const int* parent, const int* depth, const int* n_nodes, int batch,
+                             int N, int* status, hipStream_t stream);
 hipError_t launch_tree_root(const int* root_token, const int* ctx_len, int batch, int N,
                             int* parent, int* token, int* depth, int* pos, double* score,
                             uint64_t* anc, int* n_nodes, hipStream_t stream);
