@@ -116,7 +116,10 @@ int tv_version(void);
  *   n_nodes       int32 [batch]
  *   Rows past n_nodes: parent = token = depth = pos = -1, score 0, mask 0.
  * Limits: 1 <= K <= 64, 1 <= topk <= min(64, V), V <= 2^18, 0 <= budget <= 1023,
- *   build_temp > 0, K * topk <= 4096.
+ *   build_temp > 0, K * topk <= 4096, ceil(V / 8192) * topk <= 2048, and the
+ *   selection's lists within 159 KB of LDS (TV_ERR_UNSUPPORTED beyond): every
+ *   budget up to 1023 with topk <= 16, up to 1013 with topk 32 and K 64, up
+ *   to 869 with topk 64 and K 64.
  * ------------------------------------------------------------------------ */
 size_t tv_tree_build_workspace(int batch, int K, int V, int topk, int budget);
 tv_status tv_tree_build(const void *draft_logits, tv_dtype dt, int batch, int K, int V,

@@ -82,6 +82,7 @@ def _build(**kw):
     (dict(topk=65, V=1000), tv.TV_ERR_UNSUPPORTED),
     (dict(V=(1 << 18) + 1), tv.TV_ERR_UNSUPPORTED),
     (dict(budget=1024), tv.TV_ERR_UNSUPPORTED),
+    (dict(K=64, topk=64, V=1 << 18, budget=870), tv.TV_ERR_UNSUPPORTED),  # selection LDS
     (dict(ws=None), tv.TV_ERR_WORKSPACE),
     (dict(wsb=16), tv.TV_ERR_WORKSPACE),
 ])

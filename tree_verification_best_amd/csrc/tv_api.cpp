@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr size_t kMaxSelectLds = 64 * 1024;
+constexpr size_t kMaxSelectLds = 160 * 1024 - 1024;  // a workgroup's LDS, less the static part
 constexpr int kMaxGridY = 65535;
 
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }

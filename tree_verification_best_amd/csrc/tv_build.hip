@@ -790,10 +790,20 @@ hipError_t launch_build(const BuildPlan& p, const void* draft, bool bf16, int ba
   // one workgroup per sequence; larger budgets have longer candidate lists,
   // whose counting passes gain from more waves (measured: 256 threads up to
   // budget 127, 512 up to 511, then 1024)
-#define TV_SELECT(NT)                                                                        \
-  hipLaunchKernelGGL((k_select<NT>), dim3(batch), dim3(NT), p.select_lds, stream, ftok, fq, K, \
-                     topk, budget, p.P, root_token, ctx_len, parent, token, depth, pos, score,  \
-                     anc, n_nodes)
+  // the selection's lists live in dynamic LDS, beyond 64 KB for large
+  // budgets (gfx950 gives a workgroup up to 160 KB once the kernel allows it)
+#define TV_SELECT(NT)                                                                          \
+  do {                                                                                         \
+    if (p.select_lds > 65536) {                                                                \
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_select<NT>),   \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,     \
+                                               (int)p.select_lds);                             \
+      if (e != hipSuccess) return e;                                                           \
+    }                                                                                          \
+    hipLaunchKernelGGL((k_select<NT>), dim3(batch), dim3(NT), p.select_lds, stream, ftok, fq,  \
+                       K, topk, budget, p.P, root_token, ctx_len, parent, token, depth, pos,    \
+                       score, anc, n_nodes);                                                   \
+  } while (0)
   if (budget < 128)
     TV_SELECT(256);
   else if (budget < 512)
