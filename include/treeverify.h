@@ -7,12 +7,15 @@
  *   tv_tree_attention_verify tree-masked attention of the target over
  *                            context + tree (one layer)
  *   tv_tree_accept           acceptance walk -> accepted path + one token
- * plus tv_tree_ancestors and tv_tree_check for trees that come from
- * elsewhere, tv_tree_root and
- * tv_tree_expand (a layer-wise builder: root, then one call per drafting
- * step), tv_tree_budget (cost-aware tree size), tv_kv_commit (keep the
- * accepted path in the KV cache) and the rotary-embedding variants
- * tv_tree_attention_verify_rope and tv_kv_commit_rope.
+ * plus:
+ *   tv_tree_ancestors, tv_tree_check   trees that come from elsewhere
+ *   tv_tree_root, tv_tree_expand       a layer-wise builder (root, then one
+ *                                      call per drafting step)
+ *   tv_tree_budget                     cost-aware tree size
+ *   tv_kv_commit                       keep the accepted path in the KV cache
+ *   tv_tree_attention_verify_rope, tv_kv_commit_rope
+ *                                      the same with the rotary embedding
+ *                                      applied at the tree's position ids
  *
  * Conventions shared by every call
  *   - Every array argument is a DEVICE pointer owned by the caller, dense
@@ -21,7 +24,9 @@
  *     `workspace` of at least the size the matching *_workspace() returns.
  *   - Calls are asynchronous on `stream`: they enqueue kernels and return
  *     without synchronising.  The library keeps no global mutable state, so
- *     calls from several host threads on different streams are safe.
+ *     calls from several host threads on different streams are safe (for
+ *     large budgets tv_tree_build raises its selection kernel's dynamic-LDS
+ *     limit in the HIP runtime, an idempotent setting).
  *   - Arguments are checked on the host before any launch; a bad argument
  *     returns TV_ERR_INVALID (or TV_ERR_UNSUPPORTED for a valid request this
  *     build does not serve) and launches nothing.  A launch failure
