@@ -64,11 +64,12 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 
-// Work items are (sequence x KV head, row tile, split) with the split fastest.
-// Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
-// XCD w % 8), so workgroup w takes item (w % 8) * per + w / 8: every XCD gets
-// a contiguous range of items, i.e. all the splits of a few (KV head, row
-// tile) pairs, and the Q rows and K/V of a head stay in one XCD's L2.
+// Work items are (sequence x KV head, split, row tile).  Workgroups are
+// dispatched round-robin over the 8 XCDs (workgroup w runs on XCD w % 8).
+// The row tiles of one (KV head, split) read the same K/V tiles, so they run
+// on one XCD and share its L2; consecutive (KV head, split) units go to
+// different XCDs, so that sequences of different context lengths spread over
+// all of them.
 //
 // Within a workgroup, the kAttnKH waves of one row block take the kAttnKH
 // 64-key quarters of every staged tile (two waves per SIMD), each with its own
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int* __restrict__ ctx_len,
     const uint64_t* __restrict__ anc, const int* __restrict__ n_nodes, int N, int Hq, int Hkv,
-    int cap, int S, int KS, int MT, int items, float scale_log2, uint16_t* __restrict__ Opart,
+    int cap, int S, int KS, int MT, int units, float scale_log2, uint16_t* __restrict__ Opart,
     float* __restrict__ Mpart, float* __restrict__ Lpart, int batch, const int* __restrict__ pos,
     double log2_base) {
   constexpr int KP = D + 8;   // K tile pitch (bf16): 16-byte reads spread over banks
@@ -93,13 +94,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
   __shared__ double Rt[ROPE ? D / 2 : 1];         // rotary rate of each pair
   __shared__ int Pk[ROPE ? 1024 : 1];             // position ids of the tree keys
 
+  // unit u = (sequence x KV head, split), split fastest, goes to XCD u % 8;
+  // the XCD's workgroups w = x, x + 8, ... take its units in order, MT
+  // row tiles each
   const int w = blockIdx.x;
-  const int per = (items + 7) / 8;
-  const int item = (w % 8) * per + w / 8;
-  if (item >= items) return;  // whole workgroup, before any barrier
-  const int split = item % (S + 1);
-  const int mt = (item / (S + 1)) % MT;
-  const int bg = item / ((S + 1) * MT);
+  const int j = w / 8;
+  const int u = w % 8 + 8 * (j / MT);
+  if (u >= units) return;  // whole workgroup, before any barrier
+  const int mt = j % MT;
+  const int split = u % (S + 1);
+  const int bg = u / (S + 1);
   const int b = bg / Hkv, g = bg % Hkv;
   const int G = Hq / Hkv;
   // ctx_len <= max_ctx and max_ctx + N <= cap are preconditions; the clamp
@@ -745,15 +749,15 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, con
   float* Mpart = reinterpret_cast<float*>(w + p.off_ml);
   float* Lpart = Mpart + prow;
   const float scale_log2 = scale * 1.4426950408889634f;
-  const int items = batch * Hkv * p.mtiles * (p.splits + 1);
-  const int grid = 8 * ((items + 7) / 8);
+  const int units = batch * Hkv * (p.splits + 1);
+  const int grid = 8 * ((units + 7) / 8) * p.mtiles;
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
 #define TV_PARTIAL(DD, R)                                                                   \
   hipLaunchKernelGGL((k_attn_partial<DD, R>), dim3(grid), dim3(kAttnThreads), 0, stream, q16, \
                      k16, v16, ctx_len, anc, n_nodes, N, Hq, Hkv, cap, p.splits,              \
-                     p.keys_per_split, p.mtiles, items, scale_log2, Opart, Mpart, Lpart, batch, \
+                     p.keys_per_split, p.mtiles, units, scale_log2, Opart, Mpart, Lpart, batch, \
                      pos, log2_base)
   if (D == 128) {
     if (rope)
