@@ -686,10 +686,13 @@ AttnPlan attention_plan(int batch, int N, int Hq, int Hkv, int D, int max_ctx, i
   if (S <= 0) {
     // A cost model fitted to measured times on the 256-CU part: one
     // workgroup per CU at a time, each paying a fixed ~13 us (launch,
-    // prologue loads, partial stores) plus ~1 us per 64-key tile, in
-    // ceil(workgroups / 256) rounds; then the combine, ~3.5 us plus its
-    // partial reads at ~5 TB/s.  Fewer splits mean longer loops, more
-    // splits more rounds and more partial traffic.
+    // prologue loads, partial stores) plus ~1 us per 64-key tile; then the
+    // combine, ~3.5 us plus its partial reads at ~5 TB/s.  One sequence
+    // runs in ceil(workgroups / 256) equal rounds.  A batch may hold
+    // contexts of any lengths up to max_ctx, so its workgroups differ and
+    // the CUs refill as they finish: the work spread over the CUs plus the
+    // longest workgroup.  Fewer splits mean longer loops, more splits more
+    // workgroups and more partial traffic.
     const int64_t wg_per_split = (int64_t)batch * Hkv * p.mtiles;
     const double part_bytes = (double)batch * N * Hq * (D * 2 + 8);
     double best = 1e300;
@@ -697,8 +700,11 @@ AttnPlan attention_plan(int batch, int N, int Hq, int Hkv, int D, int max_ctx, i
       const int tps = tiles_per_split(c);
       const int sp = (tiles_ctx + tps - 1) / tps;
       if (sp != c) continue;  // the same as a smaller count
-      const int64_t rounds = (wg_per_split * (sp + 1) + 255) / 256;
-      const double cost = rounds * (13.0 + tps) + 3.5 + part_bytes * (sp + 1) / 5e6;
+      const int64_t wgs = wg_per_split * (sp + 1);
+      const double per_wg = 13.0 + tps;
+      const double run = batch == 1 ? (double)((wgs + 255) / 256) * per_wg
+                                    : (double)wgs * per_wg / 256.0 + per_wg;
+      const double cost = run + 3.5 + part_bytes * (sp + 1) / 5e6;
       if (cost < best) {
         best = cost;
         S = c;
