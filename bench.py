@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replays of captured rounds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--round-only", action="store_true",
+                    help="time the round alone: no rotary, commit, budget, expansion or budget "
+                         "sweep calls after the steps (clean per-kernel profiles)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run 20 plain 256 MiB device-to-device copies and exit")
@@ -383,101 +386,103 @@ def main():
     calls = {}
     for name, (a, z) in (("build", (0, 1)), ("attention", (1, 2)), ("accept", (2, 3))):
         calls[name] = sum(evs[i][a].elapsed_time(evs[i][z]) for i in range(args.steps)) / args.steps
-    # verification with the rotary embedding fused (queries and tree keys
-    # turned at the tree's position ids), per call with events like the plain
-    # call, over the same input sets and the last step's tree
-    nrope = min(args.steps, 100)
-    rev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nrope)]
-    for i in range(nrope + 5):
-        s = sets[i % nsets]
-        if i >= 5:
-            rev[i - 5][0].record(stream)
-        tv.tv_tree_attention_verify(s["q"], s["k"], s["v"], s["ctx"], tree["anc"], tree["n_nodes"],
-                                    max_ctx, workspace=ws_a, out=attn_out, lse=lse,
-                                    pos=tree["pos"], rope_base=ROPE_BASE)
-        if i >= 5:
-            rev[i - 5][1].record(stream)
-    torch.cuda.synchronize()
-    calls["attention_rope"] = sum(e[0].elapsed_time(e[1]) for e in rev) / nrope
-    # the commit, outside the timed steps (acc holds the last step's walk).
-    # One call is shorter than the host's launch path, so the calls are
-    # captured into a graph and the replays timed, as device time.
-    ncommit = 50
-    cg = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(cg):
-        for i in range(ncommit):
-            commit_(i)
-    cg.replay()
-    torch.cuda.synchronize()
-    c0 = torch.cuda.Event(enable_timing=True)
-    c1 = torch.cuda.Event(enable_timing=True)
-    reps = 4
-    c0.record(stream)
-    for _ in range(reps):
+    sweep = {}
+    if not args.round_only:
+        # verification with the rotary embedding fused (queries and tree keys
+        # turned at the tree's position ids), per call with events like the plain
+        # call, over the same input sets and the last step's tree
+        nrope = min(args.steps, 100)
+        rev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nrope)]
+        for i in range(nrope + 5):
+            s = sets[i % nsets]
+            if i >= 5:
+                rev[i - 5][0].record(stream)
+            tv.tv_tree_attention_verify(s["q"], s["k"], s["v"], s["ctx"], tree["anc"], tree["n_nodes"],
+                                        max_ctx, workspace=ws_a, out=attn_out, lse=lse,
+                                        pos=tree["pos"], rope_base=ROPE_BASE)
+            if i >= 5:
+                rev[i - 5][1].record(stream)
+        torch.cuda.synchronize()
+        calls["attention_rope"] = sum(e[0].elapsed_time(e[1]) for e in rev) / nrope
+        # the commit, outside the timed steps (acc holds the last step's walk).
+        # One call is shorter than the host's launch path, so the calls are
+        # captured into a graph and the replays timed, as device time.
+        ncommit = 50
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg):
+            for i in range(ncommit):
+                commit_(i)
         cg.replay()
-    c1.record(stream)
-    torch.cuda.synchronize()
-    calls["commit"] = c0.elapsed_time(c1) / (reps * ncommit)
-    # verification time against the tree budget (the pages' time-vs-budget
-    # figure): one sequence with this workload's heads, context 4096, random
-    # trees of B + 1 nodes, per call with events
-    sweep = b_sweep(c, dev, stream)
-    if c["build"]:
-        # the cost-aware tree size over the last step's tree; the cost of n
-        # draft nodes is the measured verification time, interpolated
-        # between the sweep's budgets
-        import numpy as np
-        sb = sorted(sweep)
-        cost_h = np.interp(np.arange(N), sb, [sweep[x] for x in sb])
-        cost = torch.from_numpy(cost_h).to(dev)
-        n_out = torch.empty((b,), **i32)
-        bg = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(bg):
-            for _ in range(ncommit):
-                tv.tv_tree_budget(tree["score"], tree["n_nodes"], cost, n_nodes_out=n_out)
-        bg.replay()
         torch.cuda.synchronize()
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        reps = 4
         c0.record(stream)
         for _ in range(reps):
+            cg.replay()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        calls["commit"] = c0.elapsed_time(c1) / (reps * ncommit)
+        # verification time against the tree budget (the pages' time-vs-budget
+        # figure): one sequence with this workload's heads, context 4096, random
+        # trees of B + 1 nodes, per call with events
+        sweep = b_sweep(c, dev, stream)
+        if c["build"]:
+            # the cost-aware tree size over the last step's tree; the cost of n
+            # draft nodes is the measured verification time, interpolated
+            # between the sweep's budgets
+            import numpy as np
+            sb = sorted(sweep)
+            cost_h = np.interp(np.arange(N), sb, [sweep[x] for x in sb])
+            cost = torch.from_numpy(cost_h).to(dev)
+            n_out = torch.empty((b,), **i32)
+            bg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(bg):
+                for _ in range(ncommit):
+                    tv.tv_tree_budget(tree["score"], tree["n_nodes"], cost, n_nodes_out=n_out)
             bg.replay()
-        c1.record(stream)
-        torch.cuda.synchronize()
-        calls["budget"] = c0.elapsed_time(c1) / (reps * ncommit)
-        # a layer-wise build of the same tree capacity: tv_tree_root, then K
-        # drafting steps of tv_tree_expand at a frontier of EXPAND_W slots with
-        # top-k children, on the drafter's next-token logits (the same dtype
-        # as the draft marginals); per_call.expand is one step (the root
-        # call's share included)
-        xl = [torch.from_numpy(a).to(dev) for a in
-              workloads.expand_logits(dict(c, dtype="f32"), b, EXPAND_W, K)]
-        xtree = {f: torch.empty_like(t) for f, t in tree.items()}
-        front = torch.empty((b, EXPAND_W), **i32)
-        nxt = torch.empty((b, EXPAND_W), **i32)
-        ws_x = torch.empty(tv.tree_expand_workspace(b, EXPAND_W, V, c["k"]), dtype=torch.uint8,
-                           device=dev)
-        f0 = torch.full((b, EXPAND_W), -1, **i32)
-        f0[:, 0] = 0
+            torch.cuda.synchronize()
+            c0.record(stream)
+            for _ in range(reps):
+                bg.replay()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            calls["budget"] = c0.elapsed_time(c1) / (reps * ncommit)
+            # a layer-wise build of the same tree capacity: tv_tree_root, then K
+            # drafting steps of tv_tree_expand at a frontier of EXPAND_W slots with
+            # top-k children, on the drafter's next-token logits (the same dtype
+            # as the draft marginals); per_call.expand is one step (the root
+            # call's share included)
+            xl = [torch.from_numpy(a).to(dev) for a in
+                  workloads.expand_logits(dict(c, dtype="f32"), b, EXPAND_W, K)]
+            xtree = {f: torch.empty_like(t) for f, t in tree.items()}
+            front = torch.empty((b, EXPAND_W), **i32)
+            nxt = torch.empty((b, EXPAND_W), **i32)
+            ws_x = torch.empty(tv.tree_expand_workspace(b, EXPAND_W, V, c["k"]), dtype=torch.uint8,
+                               device=dev)
+            f0 = torch.full((b, EXPAND_W), -1, **i32)
+            f0[:, 0] = 0
 
-        def layerwise_():
-            tv.tv_tree_root(sets[0]["roots"], sets[0]["ctx"], N, out=xtree)
-            front.copy_(f0)
-            for j in range(K):
-                tv.tv_tree_expand(xl[j], c["k"], front, xtree, sets[0]["ctx"],
-                                  next_frontier=nxt, workspace=ws_x)
-                front.copy_(nxt)
+            def layerwise_():
+                tv.tv_tree_root(sets[0]["roots"], sets[0]["ctx"], N, out=xtree)
+                front.copy_(f0)
+                for j in range(K):
+                    tv.tv_tree_expand(xl[j], c["k"], front, xtree, sets[0]["ctx"],
+                                      next_frontier=nxt, workspace=ws_x)
+                    front.copy_(nxt)
 
-        layerwise_()
-        xg = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(xg):
             layerwise_()
-        xg.replay()
-        torch.cuda.synchronize()
-        c0.record(stream)
-        for _ in range(reps):
+            xg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(xg):
+                layerwise_()
             xg.replay()
-        c1.record(stream)
-        torch.cuda.synchronize()
-        calls["expand"] = c0.elapsed_time(c1) / (reps * K)
+            torch.cuda.synchronize()
+            c0.record(stream)
+            for _ in range(reps):
+                xg.replay()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            calls["expand"] = c0.elapsed_time(c1) / (reps * K)
 
     # ---- accounting ------------------------------------------------------
     nn_h = tree["n_nodes"].cpu().numpy()
