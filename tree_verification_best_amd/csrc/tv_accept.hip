@@ -198,10 +198,10 @@ __global__ __launch_bounds__(kAccNT) void k_rowz(const T* __restrict__ target,
   }
   __syncthreads();
   const float m = s_m;
-  uint64_t acc = 0;
+  double accd = (double)weight_f(x[0], m, inv_t);  // 16 weights of at most 2^44: exact
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc += weight(x[j], m, inv_t);  // -inf padding weighs 0
-  acc = wave_sum_u64(acc);
+  for (int j = 1; j < 16; ++j) accd += (double)weight_f(x[j], m, inv_t);  // -inf pads weigh 0
+  const uint64_t acc = wave_sum_u64((uint64_t)accd);
   if (lane == 0) wsum[threadIdx.x / WAVE] = acc;
   if (wtg) {
     // children whose tokens fall in this chunk (the logit is re-read: the

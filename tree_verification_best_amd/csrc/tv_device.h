@@ -19,10 +19,11 @@ constexpr int WAVE = 64;
 // n = rint(x * log2e) and ln2 split into a high part with 12 significand
 // bits (0x3f317000) and the fp32 rounding of the remainder (0x3805fdf4);
 // e^r from its Taylor series to degree 7 (coefficients fp32(1/i!)) by Horner
-// with fused multiply-adds; the result is scaled by 2^n exactly.
+// with fused multiply-adds; the result is scaled by 2^n exactly.  Written
+// without a branch: every lane evaluates the polynomial and the range test
+// selects the result (NaN and -inf inputs give 0).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float exp_spec(float x) {
-  if (!(x >= -32.0f)) return 0.0f;
   const float kLog2e = __builtin_bit_cast(float, 0x3fb8aa3bu);
   const float kLn2Hi = __builtin_bit_cast(float, 0x3f317000u);
   const float kLn2Lo = __builtin_bit_cast(float, 0x3805fdf4u);
@@ -44,17 +45,26 @@ __device__ __forceinline__ float exp_spec(float x) {
   p = __builtin_fmaf(p, r, c2);
   p = __builtin_fmaf(p, r, 1.0f);
   p = __builtin_fmaf(p, r, 1.0f);
-  return __builtin_ldexpf(p, (int)n);
+  const float e = __builtin_ldexpf(p, (int)n);
+  return x >= -32.0f ? e : 0.0f;
 }
 
 // Fixed-point weight of logit l in a row with maximum m at inverse
 // temperature inv_t: rint(exp_spec(fl32(fl32(l - m) * inv_t)) * 2^44).
-__device__ __forceinline__ uint64_t weight(float l, float m, float inv_t) {
+// weight_f returns it as an integer-valued float (exact: at most 2^44, and
+// fp32 holds every integer it rounds to); such integers also add exactly in
+// fp64 while a sum stays below 2^53, i.e. for up to 512 weights, which is
+// how the streaming kernels sum them before one conversion to uint64.
+__device__ __forceinline__ float weight_f(float l, float m, float inv_t) {
   float d = l - m;
   float x = d * inv_t;
   float e = exp_spec(x);
   float s = e * 17592186044416.0f;  // 2^44
-  return (uint64_t)__builtin_rintf(s);
+  return __builtin_rintf(s);
+}
+
+__device__ __forceinline__ uint64_t weight(float l, float m, float inv_t) {
+  return (uint64_t)weight_f(l, m, inv_t);
 }
 
 // ---------------------------------------------------------------------------
