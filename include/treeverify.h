@@ -26,7 +26,8 @@
  *     without synchronising.  The library keeps no global mutable state, so
  *     calls from several host threads on different streams are safe (for
  *     large budgets tv_tree_build raises its selection kernel's dynamic-LDS
- *     limit in the HIP runtime, an idempotent setting).
+ *     limit in the HIP runtime, an idempotent setting; the test hook
+ *     tv_debug_set_spin_limit changes a process-wide setting).
  *   - Arguments are checked on the host before any launch; a bad argument
  *     returns TV_ERR_INVALID (or TV_ERR_UNSUPPORTED for a valid request this
  *     build does not serve) and launches nothing.  A launch failure
@@ -85,6 +86,13 @@ const char *tv_status_string(tv_status s);
 
 /* ABI version: major * 10000 + minor * 100 + patch. */
 int tv_version(void);
+
+/* Test hook: the number of polls a block of tv_tree_accept's sampled row
+ * pass makes while waiting for the other blocks of its row before it finds
+ * the row maximum by itself (< 0 restores the default, 4096; larger values
+ * are capped there).  0 sends nearly every block down that path, which
+ * gives the same results.  Process-wide; returns the previous value. */
+int tv_debug_set_spin_limit(int polls);
 
 /* ------------------------------------------------------------------------
  * tv_tree_build -- draft tree from per-position draft marginals.
@@ -285,6 +293,12 @@ tv_status tv_tree_attention_verify_rope(const void *q, const void *k_cache, cons
  * are never accepted.
  * Limits: V <= 2^18; N <= 1024; 1 <= max_depth <= 1023; temperature > 0 in
  * sampled mode; 1 <= K <= 64 with draft_logits in DRAFT mode.
+ * Sampled mode reads every logit row once: the blocks that hold the chunks
+ * of one row wait for each other to agree on the row's maximum before they
+ * weigh their chunks.  The grid is sized within what the device holds at
+ * once, and the wait is bounded: a block that waits too long (other
+ * work holding the device) re-reads its row to find the maximum itself, with
+ * the same result, only slower.
  * ------------------------------------------------------------------------ */
 size_t tv_tree_accept_workspace(int batch, int N, int K, int V, tv_accept_mode mode,
                                 tv_proposal proposal);

@@ -20,7 +20,7 @@ def _declared():
 
 def test_header_functions_exported():
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 18
     lib = ctypes.CDLL(tv.LIBPATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -274,3 +274,12 @@ def test_check_rejects():
     assert L.tv_tree_check(FAKE, None, FAKE, 0, 8, FAKE, None) == tv.TV_ERR_INVALID
     assert L.tv_tree_check(FAKE, None, FAKE, 1, 0, FAKE, None) == tv.TV_ERR_INVALID
     assert L.tv_tree_check(FAKE, None, FAKE, 1, 8, None, None) == tv.TV_ERR_INVALID
+
+
+def test_spin_limit_hook():
+    """The sampled row pass's wait bound: set, capped at the default, restored."""
+    L = tv.lib()
+    assert L.tv_debug_set_spin_limit(0) == 4096
+    assert L.tv_debug_set_spin_limit(10 ** 9) == 0
+    assert L.tv_debug_set_spin_limit(-1) == 4096  # capped at the default
+    assert L.tv_debug_set_spin_limit(-1) == 4096

@@ -222,3 +222,40 @@ def test_accept_replayable():
     torch.cuda.synchronize()
     for f in a:
         assert torch.equal(a[f], b[f])
+
+
+@pytest.mark.parametrize("proposal", ["point_mass", "draft"])
+def test_accept_row_pass_fallback(proposal):
+    """The sampled row pass with its wait bound at 0 polls: nearly every block
+    finds its row's maximum by reading the whole row itself.  The results are
+    those of the oracle (and of the default bound)."""
+    r = np.random.default_rng(11)
+    V = 151936
+    if proposal == "point_mass":
+        b, N = 2, 65
+        parent, token, depth, n = _random_trees(r, b, N, V, 8, ns=[N, 40])
+        target = workloads.plant((r.standard_normal((b, N, V)) * 3).astype(np.float32),
+                                 parent, token, n, 12.0)
+        draft, kw = None, dict(max_depth=int(depth.max()) + 1)
+    else:
+        b, K = 3, 6
+        N = K + 1
+        base = (r.standard_normal((b, N, V)) * 2).astype(np.float32)
+        target = base + (0.3 * r.standard_normal((b, N, V))).astype(np.float32)
+        draft = base[:, :K] + r.standard_normal((b, K, V)).astype(np.float32)
+        parent = np.tile(np.arange(-1, N - 1, dtype=np.int32), (b, 1))
+        depth = np.tile(np.arange(N, dtype=np.int32), (b, 1))
+        token = r.integers(0, V, size=(b, N)).astype(np.int32)
+        for s in range(b):
+            for j in range(K):
+                token[s, j + 1] = int(np.argmax(draft[s, j]))
+        n = np.full(b, N, np.int32)
+        kw = dict(max_depth=K, proposal=oracle.DRAFT)
+    old = tv.lib().tv_debug_set_spin_limit(0)
+    try:
+        for T, rnd in ((1.0, 1), (0.8, 2)):
+            g, o = _both(target, parent, token, depth, n, mode=oracle.SAMPLED, draft=draft,
+                         temperature=T, seed=4321, round=rnd, **kw)
+            assert_accept_equal(g, o, f"{proposal} fallback T={T}")
+    finally:
+        tv.lib().tv_debug_set_spin_limit(old)

@@ -39,7 +39,8 @@ EXPORTS = ("tv_status_string", "tv_version", "tv_tree_build_workspace", "tv_tree
            "tv_tree_ancestors", "tv_tree_attention_workspace", "tv_tree_attention_verify",
            "tv_tree_accept_workspace", "tv_tree_accept", "tv_tree_budget", "tv_kv_commit",
            "tv_tree_root", "tv_tree_expand_workspace", "tv_tree_expand",
-           "tv_tree_attention_verify_rope", "tv_kv_commit_rope", "tv_tree_check")
+           "tv_tree_attention_verify_rope", "tv_kv_commit_rope", "tv_tree_check",
+           "tv_debug_set_spin_limit")
 
 _lib = None
 
@@ -65,6 +66,8 @@ def _load():
     L.tv_status_string.restype = c.c_char_p
     L.tv_version.argtypes = []
     L.tv_version.restype = i32
+    L.tv_debug_set_spin_limit.argtypes = [i32]
+    L.tv_debug_set_spin_limit.restype = i32
     L.tv_tree_build_workspace.argtypes = [i32, i32, i32, i32, i32]
     L.tv_tree_build_workspace.restype = sz
     L.tv_tree_build.argtypes = [vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp,

@@ -8,12 +8,17 @@
 // mass, so the residual after rejecting token t is p with t removed.
 //
 // Kernels:
-//   k_rowmax       grid (chunks, rows)  (max, argmax) of each 4096-token chunk
-//                                       of every target row (and draft row in
-//                                       DRAFT mode), stored chunk-major
-//   k_rowz         grid (chunks, rows)  fixed-point softmax mass of each chunk,
-//                                       and the weight of each child's token
-//                                       that falls in the chunk (sampled modes)
+//   k_rowmax       grid (chunks, rows)  greedy: (max, argmax) of each
+//                                       4096-token chunk of every target row,
+//                                       stored chunk-major
+//   k_zero_slots   grid (rows * Cb)     sampled: clears the row pass's slots
+//   k_rowstat      grid (J * Cb)        sampled: one pass over every target
+//                                       row (and draft row in DRAFT mode) that
+//                                       keeps its span of the row in registers
+//                                       while the row's maximum is agreed on,
+//                                       then the chunks' maxima, fixed-point
+//                                       softmax masses and the weight of each
+//                                       child's token, chunk-major
 //   k_walk         grid (batch)         gathers the tree, the row statistics,
 //                                       the children's weights and every Philox
 //                                       draw into LDS, decides every node in
@@ -26,6 +31,9 @@
 // The passes read every row; the walk only ever visits rows < n_nodes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
+#include <atomic>
 
 #include "tv_device.h"
 #include "tv_internal.h"
@@ -55,22 +63,23 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // ---------------------------------------------------------------------------
-// Vector loads of a 4096-token chunk: thread t holds tokens
-// [base + t*16, base + t*16 + 16) (16 consecutive tokens, ids ascending).
-// fp32 rows load 4 x 16 bytes, bf16 rows 2 x 16 bytes, all issued before use.
-// Tokens past the end of the row are -inf.
+// Vector loads of E * 256 tokens of a row: thread t holds tokens
+// [base + t*E, base + t*E + E) (E consecutive tokens, ids ascending), E a
+// multiple of 16.  fp32 rows load E/4 x 16 bytes, bf16 rows E/8 x 16 bytes,
+// all issued before use.  Tokens past the end of the row are -inf.
 template <typename T>
 struct ChunkLoad;
 template <>
 struct ChunkLoad<float> {
-  static __device__ __forceinline__ void load(const float* p, int base, int V, float (&x)[16]) {
-    const int i0 = base + (int)threadIdx.x * 16;
-    if (i0 + 16 <= V && (V & 3) == 0) {
-      float4 a[4];
+  template <int E>
+  static __device__ __forceinline__ void load(const float* p, int base, int V, float (&x)[E]) {
+    const int i0 = base + (int)threadIdx.x * E;
+    if (i0 + E <= V && (V & 3) == 0) {
+      float4 a[E / 4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const float4*>(p + i0 + 4 * j);
+      for (int j = 0; j < E / 4; ++j) a[j] = *reinterpret_cast<const float4*>(p + i0 + 4 * j);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < E / 4; ++j) {
         x[4 * j] = a[j].x;
         x[4 * j + 1] = a[j].y;
         x[4 * j + 2] = a[j].z;
@@ -78,21 +87,22 @@ struct ChunkLoad<float> {
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) x[j] = i0 + j < V ? p[i0 + j] : -__builtin_inff();
+      for (int j = 0; j < E; ++j) x[j] = i0 + j < V ? p[i0 + j] : -__builtin_inff();
     }
   }
 };
 template <>
 struct ChunkLoad<uint16_t> {
+  template <int E>
   static __device__ __forceinline__ void load(const uint16_t* p, int base, int V,
-                                              float (&x)[16]) {
-    const int i0 = base + (int)threadIdx.x * 16;
-    if (i0 + 16 <= V && (V & 7) == 0) {
-      uint4 a[2];
+                                              float (&x)[E]) {
+    const int i0 = base + (int)threadIdx.x * E;
+    if (i0 + E <= V && (V & 7) == 0) {
+      uint4 a[E / 8];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) a[j] = *reinterpret_cast<const uint4*>(p + i0 + 8 * j);
+      for (int j = 0; j < E / 8; ++j) a[j] = *reinterpret_cast<const uint4*>(p + i0 + 8 * j);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < E / 8; ++j) {
         const uint32_t w[4] = {a[j].x, a[j].y, a[j].z, a[j].w};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
@@ -102,16 +112,16 @@ struct ChunkLoad<uint16_t> {
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
+      for (int j = 0; j < E; ++j)
         x[j] = i0 + j < V ? bf16_to_f32(p[i0 + j]) : -__builtin_inff();
     }
   }
 };
 
 // (max, argmax lowest id) of each 4096-token chunk of every row, stored at
-// [chunk][row].  Rows past n_nodes are read too (they are inside the array)
-// and never used.  Without ARG only the maximum is kept.
-template <typename T, bool ARG>
+// [chunk][row] (greedy mode).  Rows past n_nodes are read too (they are
+// inside the array) and never used.
+template <typename T>
 __global__ __launch_bounds__(kAccNT) void k_rowmax(const T* __restrict__ target,
                                                   const T* __restrict__ draft, int V,
                                                   int64_t trows, int64_t rows,
@@ -127,85 +137,55 @@ __global__ __launch_bounds__(kAccNT) void k_rowmax(const T* __restrict__ target,
   ChunkLoad<T>::load(p, base, V, x);
   float bv = x[0];
   int bi = base + (int)threadIdx.x * 16;
-  if (ARG) {
 #pragma unroll
-    for (int j = 1; j < 16; ++j)
-      if (x[j] > bv) {  // strict: the lowest id among equal values stays
-        bv = x[j];
-        bi = base + (int)threadIdx.x * 16 + j;
-      }
-    if (bi >= V) bi = 0x7fffffff;
-    wave_argmax(bv, bi);
-  } else {
-#pragma unroll
-    for (int j = 1; j < 16; ++j) bv = fmaxf(bv, x[j]);
-    bv = wave_max_f(bv);
-  }
+  for (int j = 1; j < 16; ++j)
+    if (x[j] > bv) {  // strict: the lowest id among equal values stays
+      bv = x[j];
+      bi = base + (int)threadIdx.x * 16 + j;
+    }
+  if (bi >= V) bi = 0x7fffffff;
+  wave_argmax(bv, bi);
   if (lane_id() == 0) {
     sv[threadIdx.x / WAVE] = bv;
     si[threadIdx.x / WAVE] = bi;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < kAccNT / WAVE; ++w) {
-      if (ARG) {
-        if (vi_better(sv[w], si[w], bv, bi)) {
-          bv = sv[w];
-          bi = si[w];
-        }
-      } else {
-        bv = fmaxf(bv, sv[w]);
+    for (int w = 1; w < kAccNT / WAVE; ++w)
+      if (vi_better(sv[w], si[w], bv, bi)) {
+        bv = sv[w];
+        bi = si[w];
       }
-    }
     cmax[(int64_t)c * rows + r] = bv;
-    if (ARG) carg[(int64_t)c * rows + r] = bi;
+    carg[(int64_t)c * rows + r] = bi;
   }
 }
 
-// Fixed-point softmax mass of each chunk, at [chunk][row].  The chunk's
-// logits are loaded first; the row maximum (from the chunk maxima) arrives
-// while they are in flight.
-// With the tree given (wtg non-null), the block also stores the weight of
-// every child's token that falls in its chunk: wtg[b][x] = W of token(x) in
-// the row of parent(x); in DRAFT mode (wqg non-null) a draft row's block
-// stores wqg[b][x] = W of token(x) in draft row depth(x) - 1.
-template <typename T>
-__global__ __launch_bounds__(kAccNT) void k_rowz(const T* __restrict__ target,
-                                                const T* __restrict__ draft, int V, int C,
-                                                int64_t trows, int64_t rows, float inv_t,
-                                                const float* __restrict__ cmax,
-                                                uint64_t* __restrict__ cz, int N, int K,
-                                                const int* __restrict__ parent,
-                                                const int* __restrict__ token,
-                                                const int* __restrict__ depth,
-                                                const int* __restrict__ n_nodes,
-                                                uint64_t* __restrict__ wtg,
-                                                uint64_t* __restrict__ wqg) {
-  __shared__ float s_m;
-  __shared__ uint64_t wsum[kAccNT / WAVE];
-  const int c = blockIdx.x;
-  const int64_t r = blockIdx.y;
-  const int lane = lane_id();
-  const T* p = row_ptr(target, draft, r, trows, V);
-  const int base = c * kAcceptChunk;
-  float x[16];
-  ChunkLoad<T>::load(p, base, V, x);
-  if (threadIdx.x < WAVE) {
-    float m = -__builtin_inff();
-    for (int j = lane; j < C; j += WAVE) m = fmaxf(m, cmax[(int64_t)j * rows + r]);
-    m = wave_max_f(m);
-    if (lane == 0) s_m = m;
-  }
-  __syncthreads();
-  const float m = s_m;
-  double accd = (double)weight_f(x[0], m, inv_t);  // 16 weights of at most 2^44: exact
+// Fixed-point softmax mass of the E/16 chunks of 4096 tokens that the block
+// holds of row r (x from ChunkLoad at base = cb * E * 256, m: the row
+// maximum), stored at cz[c][r] for each chunk c < C.  With the tree given
+// (wtg non-null), the block also stores the weight of every child's token
+// that falls in its tokens: wtg[b][x] = W of token(x) in the row of
+// parent(x); in DRAFT mode (wqg non-null) a draft row's block stores
+// wqg[b][x] = W of token(x) in draft row depth(x) - 1.  Ends with a barrier.
+template <typename T, int E>
+__device__ __forceinline__ void chunk_mass(const float (&x)[E], const T* p, int V, int C, int cb,
+                                           int64_t r, int64_t trows, int64_t rows, float m,
+                                           float inv_t, uint64_t* wsum, uint64_t* cz, int N,
+                                           int K, const int* parent, const int* token,
+                                           const int* depth, const int* n_nodes,
+                                           uint64_t* wtg, uint64_t* wqg) {
+  static_assert(E % 16 == 0 && E <= 512, "fp64 partial sums must stay exact");
+  constexpr int kSpan = E * kAccNT;
+  const int base = cb * kSpan;
+  double accd = (double)weight_f(x[0], m, inv_t);  // E weights of at most 2^44: exact
 #pragma unroll
-  for (int j = 1; j < 16; ++j) accd += (double)weight_f(x[j], m, inv_t);  // -inf pads weigh 0
+  for (int j = 1; j < E; ++j) accd += (double)weight_f(x[j], m, inv_t);  // -inf pads weigh 0
   const uint64_t acc = wave_sum_u64((uint64_t)accd);
-  if (lane == 0) wsum[threadIdx.x / WAVE] = acc;
+  if (lane_id() == 0) wsum[threadIdx.x / WAVE] = acc;
   if (wtg) {
-    // children whose tokens fall in this chunk (the logit is re-read: the
-    // block has just brought the chunk into the cache)
+    // children whose tokens fall in the block's span (the logit is re-read:
+    // the block has just brought it into the cache)
     const bool trow = r < trows;
     if (trow || wqg) {
       const int64_t j = trow ? r : r - trows;
@@ -218,18 +198,166 @@ __global__ __launch_bounds__(kAccNT) void k_rowz(const T* __restrict__ target,
           const bool mine = trow ? parent[o + xx] == uu : depth[o + xx] == uu + 1;
           if (!mine) continue;
           const int t = token[o + xx];
-          if (t >= base && t < base + kAcceptChunk && t < V)
+          if (t >= base && t < base + kSpan && t < V)
             (trow ? wtg : wqg)[o + xx] = weight(Elem<T>::load(p, t), m, inv_t);
         }
       }
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t z = 0;
-    for (int w = 0; w < kAccNT / WAVE; ++w) z += wsum[w];
-    cz[(int64_t)c * rows + r] = z;
+  // chunk k of the span is held by waves [k * W4, (k + 1) * W4)
+  constexpr int kWaves = kAccNT / WAVE, W4 = kWaves / (E / 16);
+  if ((int)threadIdx.x < E / 16) {
+    const int k = threadIdx.x, c = cb * (E / 16) + k;
+    if (c < C) {
+      uint64_t z = 0;
+      for (int w = k * W4; w < (k + 1) * W4; ++w) z += wsum[w];
+      cz[(int64_t)c * rows + r] = z;
+    }
   }
+  __syncthreads();  // wsum is reused by the block's next row
+}
+
+// One pass over the rows for the sampled walks: each logit is read once and
+// kept in registers while its row's maximum is agreed on.  A block holds
+// E * 256 tokens (E / 16 chunks of 4096) of a row; Cb = ceil(V / (E * 256))
+// blocks cover a row.  Block g takes span cb = g % Cb of rows g / Cb,
+// g / Cb + J, g / Cb + 2J, ... (J = gridDim.x / Cb groups).  For each row
+// the block posts its maximum in the row's slot cb, waits until all Cb
+// slots of the row are posted, takes the row maximum and weighs its span
+// (chunk_mass).  A block with several rows (J < rows) either loads and posts
+// its next row after weighing the current one, or (PIPE) pipelines one row
+// deep: the next row's span is loaded during the wait and posted before the
+// current span is weighed.
+//
+// Slots: slot[r * slot_stride + cb] = 2^32 | bits of the span maximum, an
+// agent-scope atomic store; a reader's wave polls the row's Cb slots with
+// agent-scope atomic loads until every one is posted.  One store and one
+// load per hand-off, no cache-wide maintenance.  The maxima of the 4096-token
+// chunks also go to cmax[c][r] for the walk.
+//
+// The wait needs the Cb blocks of a group resident together; the host sizes
+// the grid within what the device holds at once.  The wait is bounded all
+// the same: a block that has polled spin_limit times in vain (other work
+// holding the device, say) takes the row maximum from the whole row itself,
+// which gives the same value, so the results never depend on the schedule.
+// The slots must be zero at the start (k_zero_slots runs first); each row's
+// slots start on a 256-byte line of their own.
+template <int E>
+__device__ __forceinline__ void post_span_max(const float (&x)[E], float* sv, float* cmax,
+                                              uint64_t* slot, int C, int cb, int64_t r,
+                                              int64_t rows, int slot_stride) {
+  float bv = x[0];
+#pragma unroll
+  for (int j = 1; j < E; ++j) bv = fmaxf(bv, x[j]);
+  bv = wave_max_f(bv);
+  if (lane_id() == 0) sv[threadIdx.x / WAVE] = bv;
+  __syncthreads();
+  constexpr int kWaves = kAccNT / WAVE, W4 = kWaves / (E / 16);
+  if (threadIdx.x == 0) {
+    float all = -__builtin_inff();
+    for (int k = 0; k < E / 16; ++k) {
+      float ck = sv[k * W4];
+      for (int w = k * W4 + 1; w < (k + 1) * W4; ++w) ck = fmaxf(ck, sv[w]);
+      const int c = cb * (E / 16) + k;
+      if (c < C) cmax[(int64_t)c * rows + r] = ck;
+      all = fmaxf(all, ck);
+    }
+    const uint64_t v = (1ull << 32) | __builtin_bit_cast(uint32_t, all);
+    __hip_atomic_store(&slot[r * slot_stride + cb], v, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <typename T, int E, bool PIPE>
+__global__ __launch_bounds__(kAccNT) void k_rowstat(const T* __restrict__ target,
+                                                   const T* __restrict__ draft, int V, int C,
+                                                   int Cb, int64_t trows, int64_t rows,
+                                                   float inv_t, float* __restrict__ cmax,
+                                                   uint64_t* slot, int slot_stride,
+                                                   uint64_t* __restrict__ cz, int N, int K,
+                                                   const int* __restrict__ parent,
+                                                   const int* __restrict__ token,
+                                                   const int* __restrict__ depth,
+                                                   const int* __restrict__ n_nodes,
+                                                   uint64_t* __restrict__ wtg,
+                                                   uint64_t* __restrict__ wqg,
+                                                   int spin_limit) {
+  __shared__ float sv[kAccNT / WAVE];
+  __shared__ float sl[kAccNT / WAVE];
+  __shared__ uint64_t wsum[kAccNT / WAVE];
+  __shared__ float s_m;
+  __shared__ int s_late;
+  constexpr int kSpan = E * kAccNT;
+  const int cb = (int)(blockIdx.x % (unsigned)Cb);
+  const int64_t J = gridDim.x / (unsigned)Cb;
+  const int lane = lane_id();
+  int64_t r = blockIdx.x / (unsigned)Cb;
+  if (r >= rows) return;
+  float x[E];
+  ChunkLoad<T>::load(row_ptr(target, draft, r, trows, V), cb * kSpan, V, x);
+  post_span_max(x, sv, cmax, slot, C, cb, r, rows, slot_stride);
+  for (; r < rows; r += J) {
+    const T* p = row_ptr(target, draft, r, trows, V);
+    const int64_t rn = r + J;
+    float y[PIPE ? E : 1];
+    if constexpr (PIPE) {
+      if (rn < rows) ChunkLoad<T>::load(row_ptr(target, draft, rn, trows, V), cb * kSpan, V, y);
+    }
+    if (threadIdx.x < WAVE) {
+      // lane j < Cb watches slot j of the row
+      const uint64_t* mine = slot + r * slot_stride + min(lane, Cb - 1);
+      uint64_t v = 0;
+      int late = 0, spins = 0;
+      while (true) {
+        v = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__all((v >> 32) != 0)) break;
+        if (spins >= spin_limit) {
+          late = 1;
+          break;
+        }
+        ++spins;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      const float m = late ? -__builtin_inff()
+                           : wave_max_f(__builtin_bit_cast(float, (uint32_t)v));
+      if (lane == 0) {
+        s_m = m;
+        s_late = late;
+      }
+    }
+    __syncthreads();
+    float m = s_m;
+    if (s_late) {  // the whole row, by this block alone
+      float mm = -__builtin_inff();
+      for (int i = (int)threadIdx.x; i < V; i += kAccNT) mm = fmaxf(mm, Elem<T>::load(p, i));
+      mm = wave_max_f(mm);
+      if (lane == 0) sl[threadIdx.x / WAVE] = mm;
+      __syncthreads();
+      m = sl[0];
+      for (int w = 1; w < kAccNT / WAVE; ++w) m = fmaxf(m, sl[w]);
+    }
+    if constexpr (PIPE) {
+      if (rn < rows) post_span_max(y, sv, cmax, slot, C, cb, rn, rows, slot_stride);
+    }
+    chunk_mass<T, E>(x, p, V, C, cb, r, trows, rows, m, inv_t, wsum, cz, N, K, parent, token,
+                     depth, n_nodes, wtg, wqg);
+    if (rn < rows) {
+      if constexpr (PIPE) {
+#pragma unroll
+        for (int j = 0; j < E; ++j) x[j] = y[j];
+      } else {
+        ChunkLoad<T>::load(row_ptr(target, draft, rn, trows, V), cb * kSpan, V, x);
+        post_span_max(x, sv, cmax, slot, C, cb, rn, rows, slot_stride);
+      }
+    }
+  }
+}
+
+// zeroes the Cb slots of every row (rows of `stride` words)
+__global__ void k_zero_slots(uint64_t* __restrict__ slot, int64_t rows, int Cb, int stride) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < rows * Cb) slot[(i / Cb) * stride + i % Cb] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -881,8 +1009,81 @@ AcceptPlan accept_plan(int batch, int N, int K, int V, bool sampled, bool draft)
   p.off_wqg = draft ? take((size_t)batch * N * sizeof(uint64_t)) : 0;
   p.off_rcz = draft ? take((size_t)batch * kMaxChunks * sizeof(uint64_t)) : 0;
   p.off_pend = draft ? take((size_t)batch * sizeof(DraftPending)) : 0;
+  p.slot_stride = (p.C + 31) & ~31;  // 256-byte rows of slots
+  p.off_slot = sampled ? take((size_t)p.rows * p.slot_stride * sizeof(uint64_t)) : 0;
   p.workspace = off;
   return p;
+}
+
+// Polls of the row-maximum wait before a k_rowstat block reads the whole row
+// itself (about 1 us each).  tv_debug_set_spin_limit lowers it so that tests
+// take the fallback.
+constexpr int kSpinLimit = 1 << 12;
+std::atomic<int> g_rowstat_spin_limit{kSpinLimit};
+
+int set_rowstat_spin_limit(int polls) {
+  const int old = g_rowstat_spin_limit.load();
+  g_rowstat_spin_limit.store(polls < 0 ? kSpinLimit : std::min(polls, kSpinLimit));
+  return old;
+}
+
+// Blocks of one k_rowstat instance the device holds at once (cached per
+// device).
+template <typename T, int E, bool PIPE>
+static int64_t rowstat_capacity() {
+  static std::atomic<int> resident[64];
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  std::atomic<int>& slot = resident[dev & 63];
+  int cap = slot.load(std::memory_order_relaxed);
+  if (cap == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&k_rowstat<T, E, PIPE>), kAccNT, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        per_cu < 1 || cus < 1) {
+      per_cu = 1;
+      cus = 64;
+    }
+    cap = per_cu * cus;
+    slot.store(cap, std::memory_order_relaxed);
+  }
+  return cap;
+}
+
+// The row pass's shape: one row per block when the device holds all the
+// (row, 8192-token span) blocks at once, else all the (row, 4096-token
+// chunk) blocks; else the pipelined kernel over 4096-token chunks with J
+// groups of Cb blocks within what the device holds, as many groups as keep
+// the rows balanced (ceil(rows / J) each).  (Measured on the 4B/8B-class
+// rounds: of the multi-row forms, 8192-token spans without or with the
+// pipeline were 9 and 13 % slower than this one.)
+struct RowstatShape {
+  int E;
+  bool pipe;
+  int Cb;
+  unsigned grid;
+};
+
+template <typename T, int E, bool PIPE>
+static RowstatShape rowstat_groups(int64_t rows, int Cb) {
+  int64_t J = std::max<int64_t>(1, rowstat_capacity<T, E, PIPE>() / Cb);
+  J = std::min<int64_t>(J, rows);
+  const int64_t iters = (rows + J - 1) / J;
+  J = (rows + iters - 1) / iters;
+  return {E, PIPE, Cb, (unsigned)(J * Cb)};
+}
+
+template <typename T>
+static RowstatShape rowstat_shape(int64_t rows, int V) {
+  const int cb32 = (V + 32 * kAccNT - 1) / (32 * kAccNT);
+  const int cb16 = (V + 16 * kAccNT - 1) / (16 * kAccNT);
+  if (rows * cb32 <= rowstat_capacity<T, 32, false>())
+    return {32, false, cb32, (unsigned)(rows * cb32)};
+  if (rows * cb16 <= rowstat_capacity<T, 16, false>())
+    return {16, false, cb16, (unsigned)(rows * cb16)};
+  return rowstat_groups<T, 16, true>(rows, cb16);
 }
 
 template <typename T>
@@ -904,12 +1105,25 @@ static void launch_accept_t(const AcceptPlan& p, const T* target, const T* draft
   const dim3 g(p.C, (unsigned)p.rows);
   const dim3 blk(kAccNT);
   if (sampled) {
-    hipLaunchKernelGGL((k_rowmax<T, false>), g, blk, 0, stream, target, draft, V, trows,
-                       p.rows, cmax, carg);
-    hipLaunchKernelGGL((k_rowz<T>), g, blk, 0, stream, target, draft, V, p.C, trows, p.rows,
-                       inv_t, cmax, cz, N, K, parent, token, depth, n_nodes, wtg, wqg);
+    uint64_t* slot = reinterpret_cast<uint64_t*>(w + p.off_slot);
+    const RowstatShape sh = rowstat_shape<T>(p.rows, V);
+    hipLaunchKernelGGL(k_zero_slots,
+                       dim3((unsigned)((p.rows * sh.Cb + kAccNT - 1) / kAccNT)), blk, 0, stream,
+                       slot, p.rows, sh.Cb, p.slot_stride);
+    const int spin = g_rowstat_spin_limit.load(std::memory_order_relaxed);
+#define TV_ROWSTAT(E, PIPE)                                                                    \
+  hipLaunchKernelGGL((k_rowstat<T, E, PIPE>), dim3(sh.grid), blk, 0, stream, target, draft, V, \
+                     p.C, sh.Cb, trows, p.rows, inv_t, cmax, slot, p.slot_stride, cz, N, K,    \
+                     parent, token, depth, n_nodes, wtg, wqg, spin)
+    if (sh.E == 32)
+      TV_ROWSTAT(32, false);
+    else if (!sh.pipe)
+      TV_ROWSTAT(16, false);
+    else
+      TV_ROWSTAT(16, true);
+#undef TV_ROWSTAT
   } else {
-    hipLaunchKernelGGL((k_rowmax<T, true>), g, blk, 0, stream, target, draft, V, trows, p.rows,
+    hipLaunchKernelGGL((k_rowmax<T>), g, blk, 0, stream, target, draft, V, trows, p.rows,
                        cmax, carg);
   }
 #define TV_WALK(M)                                                                            \

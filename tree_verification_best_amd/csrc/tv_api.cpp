@@ -279,6 +279,8 @@ tv_status tv_kv_commit(void* k_cache, void* v_cache, tv_dtype dt, int batch, int
                         accepted_nodes, width, false, 0.0, new_ctx_len, stream);
 }
 
+int tv_debug_set_spin_limit(int polls) { return tvk::set_rowstat_spin_limit(polls); }
+
 tv_status tv_kv_commit_rope(void* k_cache, void* v_cache, tv_dtype dt, int batch, int Hkv,
                             int cap, int D, const int32_t* ctx_len, const int32_t* accept_len,
                             const int32_t* accepted_nodes, int width, double rope_base,

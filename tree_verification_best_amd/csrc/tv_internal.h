@@ -79,10 +79,13 @@ struct AcceptPlan {
   // in its parent's row (and, DRAFT, in its drafter row) [batch][N]; DRAFT
   // residual chunk sums [batch][64] and the per-sequence hand-over record
   size_t off_cmax, off_carg, off_cz, off_wtg, off_wqg, off_rcz, off_pend;
+  size_t off_slot;   // per-row slots of the chunk maxima, one-pass statistics (sampled)
+  int slot_stride;   // slots per row (256-byte rows)
   size_t workspace;
 };
 
 AcceptPlan accept_plan(int batch, int N, int K, int V, bool sampled, bool draft);
+int set_rowstat_spin_limit(int polls);  // < 0: the default; returns the previous limit
 hipError_t launch_accept(const AcceptPlan& p, const void* target, const void* draft,
                          bool bf16, int batch, int N, int K, int V, const int* parent,
                          const int* token, const int* depth, const int* n_nodes, bool sampled,
