@@ -488,9 +488,25 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
 
 // Merge the S + 1 partials of every query row.  Partial s holds O_s / l_s in
 // fp16; its weight is 2^(m_s - M) l_s / L with L = sum_s 2^(m_s - M) l_s.
-// One thread per (row, head, 4 output columns):
-// the D/4 threads of a row read the same (m_s, l_s) words, and every load of
-// a batch of splits is issued before the first is used.
+// One thread per (row, head, 4 output columns): the D/4 threads of a row
+// read the same (m_s, l_s) words.  Up to kOne = 16 partials are loaded in one
+// round (with the sequence's node count alongside; rows past it are written
+// as zeros), so the kernel waits on memory once; more splits take batches of
+// eight, with the maximum found first.  The sum runs over s in order either
+// way.
+template <typename OutT>
+__device__ __forceinline__ void combine_add(float m, float l, uint2 h, float M, float& lsum,
+                                            float4& acc) {
+  const bool live = m != -__builtin_inff();
+  const float wgt = live ? __builtin_amdgcn_exp2f(m - M) : 0.f;
+  const float wl = wgt * l;  // the partial holds O / l
+  lsum += wl;
+  acc.x += wl * (float)__builtin_bit_cast(_Float16, (uint16_t)(h.x & 0xFFFFu));
+  acc.y += wl * (float)__builtin_bit_cast(_Float16, (uint16_t)(h.x >> 16));
+  acc.z += wl * (float)__builtin_bit_cast(_Float16, (uint16_t)(h.y & 0xFFFFu));
+  acc.w += wl * (float)__builtin_bit_cast(_Float16, (uint16_t)(h.y >> 16));
+}
+
 template <typename OutT>
 __global__ __launch_bounds__(256) void k_attn_combine(const uint16_t* __restrict__ Opart,
                                                      const float* __restrict__ Mpart,
@@ -499,7 +515,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(const uint16_t* __restrict
                                                      int N, int Hq, int D, int S1,
                                                      OutT* __restrict__ out,
                                                      float* __restrict__ lse) {
-  constexpr int kB = 8;  // splits per load batch
+  constexpr int kOne = 16;  // partials loaded in one round
+  constexpr int kB = 8;     // splits per load batch beyond that
   const int D4 = D / 4;
   const int64_t plane = (int64_t)batch * N * Hq;
   const int64_t r = (int64_t)blockIdx.x * (256 / D4) + threadIdx.x / D4;  // (b, node, head)
@@ -508,65 +525,81 @@ __global__ __launch_bounds__(256) void k_attn_combine(const uint16_t* __restrict
   const int64_t bn = r / Hq;
   const int b = (int)(bn / N), node = (int)(bn % N);
   OutT* dst = out + r * D + 4 * d4;
-  if (node >= min(n_nodes[b], N)) {
-    if constexpr (sizeof(OutT) == 2)
-      *reinterpret_cast<uint2*>(dst) = make_uint2(0u, 0u);
-    else
-      *reinterpret_cast<float4*>(dst) = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lse && d4 == 0) lse[r] = -__builtin_inff();
-    return;
-  }
+  const uint16_t* ob = Opart + r * D + 4 * d4;
+  const int nb = n_nodes[b];
   float M = -__builtin_inff();
-  for (int s0 = 0; s0 < S1; s0 += kB) {
-    float ms[kB];
-#pragma unroll
-    for (int j = 0; j < kB; ++j)
-      ms[j] = s0 + j < S1 ? Mpart[(s0 + j) * plane + r] : -__builtin_inff();
-#pragma unroll
-    for (int j = 0; j < kB; ++j) M = fmaxf(M, ms[j]);
-  }
   float lsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < S1; s0 += kB) {
-    float ms[kB], ls[kB];
-    float4 o[kB];
+  if (S1 <= kOne) {
+    float ms[kOne], ls[kOne];
+    uint2 oh[kOne];
 #pragma unroll
-    for (int j = 0; j < kB; ++j) {
-      const int s = min(s0 + j, S1 - 1);
-      ms[j] = Mpart[s * plane + r];
-      ls[j] = Lpart[s * plane + r];
-      const uint2 h = *reinterpret_cast<const uint2*>(Opart + (s * plane + r) * D + 4 * d4);
-      o[j] = make_float4((float)__builtin_bit_cast(_Float16, (uint16_t)(h.x & 0xFFFFu)),
-                         (float)__builtin_bit_cast(_Float16, (uint16_t)(h.x >> 16)),
-                         (float)__builtin_bit_cast(_Float16, (uint16_t)(h.y & 0xFFFFu)),
-                         (float)__builtin_bit_cast(_Float16, (uint16_t)(h.y >> 16)));
+    for (int j = 0; j < kOne; ++j) {
+      if (j < S1) {  // uniform
+        ms[j] = Mpart[j * plane + r];
+        ls[j] = Lpart[j * plane + r];
+        oh[j] = *reinterpret_cast<const uint2*>(ob + j * plane * D);
+      } else {
+        ms[j] = -__builtin_inff();
+        ls[j] = 0.f;
+        oh[j] = make_uint2(0u, 0u);
+      }
     }
+    if (node >= min(nb, N)) goto pad;
 #pragma unroll
-    for (int j = 0; j < kB; ++j) {
-      const bool live = s0 + j < S1 && ms[j] != -__builtin_inff();
-      const float wgt = live ? __builtin_amdgcn_exp2f(ms[j] - M) : 0.f;
-      const float wl = wgt * ls[j];  // the partial holds O / l
-      lsum += wl;
-      acc.x += wl * o[j].x;
-      acc.y += wl * o[j].y;
-      acc.z += wl * o[j].z;
-      acc.w += wl * o[j].w;
-    }
-  }
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  acc.x *= inv;
-  acc.y *= inv;
-  acc.z *= inv;
-  acc.w *= inv;
-  if constexpr (sizeof(OutT) == 2) {
-    *reinterpret_cast<uint2*>(dst) =
-        make_uint2((uint32_t)f32_to_bf16_bits(acc.x) | ((uint32_t)f32_to_bf16_bits(acc.y) << 16),
-                   (uint32_t)f32_to_bf16_bits(acc.z) | ((uint32_t)f32_to_bf16_bits(acc.w) << 16));
+    for (int j = 0; j < kOne; ++j)
+      if (j < S1) M = fmaxf(M, ms[j]);
+#pragma unroll
+    for (int j = 0; j < kOne; ++j)
+      if (j < S1) combine_add<OutT>(ms[j], ls[j], oh[j], M, lsum, acc);
   } else {
-    *reinterpret_cast<float4*>(dst) = acc;
+    if (node >= min(nb, N)) goto pad;
+    for (int s0 = 0; s0 < S1; s0 += kB) {
+      float ms[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j)
+        ms[j] = s0 + j < S1 ? Mpart[(s0 + j) * plane + r] : -__builtin_inff();
+#pragma unroll
+      for (int j = 0; j < kB; ++j) M = fmaxf(M, ms[j]);
+    }
+    for (int s0 = 0; s0 < S1; s0 += kB) {
+      float ms[kB], ls[kB];
+      uint2 oh[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const int s = min(s0 + j, S1 - 1);
+        ms[j] = Mpart[s * plane + r];
+        ls[j] = Lpart[s * plane + r];
+        oh[j] = *reinterpret_cast<const uint2*>(ob + s * plane * D);
+      }
+#pragma unroll
+      for (int j = 0; j < kB; ++j)
+        if (s0 + j < S1) combine_add<OutT>(ms[j], ls[j], oh[j], M, lsum, acc);
+    }
   }
-  if (lse && d4 == 0)
-    lse[r] = lsum > 0.f ? (M + log2f(lsum)) * 0.69314718055994531f : -__builtin_inff();
+  {
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    acc.x *= inv;
+    acc.y *= inv;
+    acc.z *= inv;
+    acc.w *= inv;
+    if constexpr (sizeof(OutT) == 2) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(
+          (uint32_t)f32_to_bf16_bits(acc.x) | ((uint32_t)f32_to_bf16_bits(acc.y) << 16),
+          (uint32_t)f32_to_bf16_bits(acc.z) | ((uint32_t)f32_to_bf16_bits(acc.w) << 16));
+    } else {
+      *reinterpret_cast<float4*>(dst) = acc;
+    }
+    if (lse && d4 == 0)
+      lse[r] = lsum > 0.f ? (M + log2f(lsum)) * 0.69314718055994531f : -__builtin_inff();
+    return;
+  }
+pad:
+  if constexpr (sizeof(OutT) == 2)
+    *reinterpret_cast<uint2*>(dst) = make_uint2(0u, 0u);
+  else
+    *reinterpret_cast<float4*>(dst) = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (lse && d4 == 0) lse[r] = -__builtin_inff();
 }
 
 // ---------------------------------------------------------------------------
