@@ -52,6 +52,9 @@ CASES = [
     ("wide", 2, 200, 3000, 1.0, 2.5, 64, "f32"),
     ("vocab-1", 2, 9, 1, 1.0, 0.0, 4, "f32"),
     ("full-vocab", 2, 65, 151936, 3.0, 12.0, 8, "f32"),
+    # 130 rows x 38 chunks: more blocks than the device holds, so the sampled
+    # row pass runs pipelined over bf16 rows
+    ("full-vocab-bf16", 2, 65, 151936, 3.0, 12.0, 8, "bf16"),
 ]
 
 
