@@ -40,6 +40,7 @@ constexpr int kTileKeys = 64;  // keys one wave takes per iteration (two 32-key 
 constexpr int kAttnWaves = 4;  // row blocks per workgroup, 32 query rows each
 constexpr int kAttnKH = 2;     // waves per row block: they split each staged tile's keys
 constexpr int kAttnThreads = kAttnWaves * WAVE * kAttnKH;
+constexpr float kRescaleSlack = 8.0f;  // log2 units: running weights stay below 2^8
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -160,6 +161,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = -__builtin_inff();
+  // in raw score units (none for a scale so small that it would overflow)
+  const float rescale_slack = scale_log2 > 1e-30f ? kRescaleSlack / scale_log2 : 0.f;
   float l_run = 0.f;
 
   const uint16_t* kbase = kc + ((int64_t)b * Hkv + g) * (int64_t)cap * D;
@@ -359,7 +362,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
 #pragma unroll
       for (int i = 0; i < 32; i += 2) tmax = fmaxf(tmax, fmaxf(x[i], x[i + 1]));
       tmax = fmaxf(tmax, xor32_f(tmax));
-      const bool grow = tmax > m_run;
+      // the reference maximum moves only when a score exceeds it by more than
+      // kRescaleSlack in the exponent (weights up to 2^kRescaleSlack are fine
+      // in fp32 and bf16), so that most tiles skip the rescale
+      const bool grow = tmax > m_run + rescale_slack;
       if (__ballot(grow)) {
         const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - tmax) * scale_log2) : 1.f;
         l_run *= alpha;
