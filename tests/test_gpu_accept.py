@@ -262,3 +262,28 @@ def test_accept_row_pass_fallback(proposal):
             assert_accept_equal(g, o, f"{proposal} fallback T={T}")
     finally:
         tv.lib().tv_debug_set_spin_limit(old)
+
+
+def test_accept_concurrent_streams():
+    """Sampled walks of the full-vocabulary shape on four streams at once, each
+    with its own workspace: together their row-pass grids exceed what the
+    device holds at once, so blocks may wait in vain and take the fallback.
+    Every stream's result is the oracle's."""
+    r = np.random.default_rng(12)
+    b, N, V = 1, 65, 151936
+    parent, token, depth, n = _random_trees(r, b, N, V, 8)
+    target = workloads.plant((r.standard_normal((b, N, V)) * 3).astype(np.float32),
+                             parent, token, n, 12.0)
+    args = (dev(target), dev(parent), dev(token), dev(depth), dev(n))
+    kw = dict(mode=tv.TV_SAMPLED, seed=77, max_depth=int(depth.max()) + 1)
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    torch.cuda.synchronize()
+    outs = []
+    for i, st in enumerate(streams):
+        with torch.cuda.stream(st):
+            outs.append(tv.tv_tree_accept(*args, round=i, **kw))
+    torch.cuda.synchronize()
+    for i, g in enumerate(outs):
+        o = oracle.tree_accept(target, parent, token, depth, n, mode=oracle.SAMPLED,
+                               seed=77, round=i, max_depth=kw["max_depth"])
+        assert_accept_equal(g, o, f"stream {i}")
