@@ -45,6 +45,9 @@ constexpr int kAccE = kAcceptChunk / kAccNT;  // 16 tokens per thread and chunk
 constexpr int kMaxN = 1024;                   // rows per sequence
 constexpr int kMaxDraftRows = 64;             // drafter positions (DRAFT proposal)
 constexpr int kMaxChunks = 64;                // chunks per row (V <= 2^18)
+// the rows' mass accumulators of the sampled row pass are one 256-byte line
+// apart, so that the blocks adding to one row do not meet other rows' there
+constexpr int kRowzStride = 32;
 
 enum WalkMode { kGreedy = 0, kPointMass = 1, kDraft = 2 };
 
@@ -275,7 +278,9 @@ __global__ __launch_bounds__(kAccNT) void k_rowstat(const T* __restrict__ target
                                                    int Cb, int64_t trows, int64_t rows,
                                                    float inv_t, float* __restrict__ cmax,
                                                    uint64_t* slot, int slot_stride,
-                                                   uint64_t* __restrict__ cz, int N, int K,
+                                                   uint64_t* __restrict__ cz,
+                                                   float* __restrict__ rowm, uint64_t* rowz,
+                                                   int N, int K,
                                                    const int* __restrict__ parent,
                                                    const int* __restrict__ token,
                                                    const int* __restrict__ depth,
@@ -342,6 +347,17 @@ __global__ __launch_bounds__(kAccNT) void k_rowstat(const T* __restrict__ target
     }
     chunk_mass<T, E>(x, p, V, C, cb, r, trows, rows, m, inv_t, wsum, cz, N, K, parent, token,
                      depth, n_nodes, wtg, wqg);
+    // the row's totals for the walk: its maximum, and its mass as the sum of
+    // the spans' masses (integer atomics, so the order does not matter).  The
+    // last wave sends them: wave 0 polls, and a wave's loads wait for its own
+    // outstanding atomics.
+    if (threadIdx.x == kAccNT - WAVE) {
+      uint64_t z = 0;
+      for (int w = 0; w < kAccNT / WAVE; ++w) z += wsum[w];
+      __hip_atomic_fetch_add(&rowz[r * kRowzStride], z, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      if (cb == 0) rowm[r] = m;
+    }
     if (rn < rows) {
       if constexpr (PIPE) {
 #pragma unroll
@@ -354,10 +370,13 @@ __global__ __launch_bounds__(kAccNT) void k_rowstat(const T* __restrict__ target
   }
 }
 
-// zeroes the Cb slots of every row (rows of `stride` words)
-__global__ void k_zero_slots(uint64_t* __restrict__ slot, int64_t rows, int Cb, int stride) {
+// zeroes the Cb slots of every row (rows of `stride` words) and the rows'
+// mass accumulators
+__global__ void k_zero_slots(uint64_t* __restrict__ slot, int64_t rows, int Cb, int stride,
+                             uint64_t* __restrict__ rowz) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < rows * Cb) slot[(i / Cb) * stride + i % Cb] = 0;
+  if (i < rows) rowz[i * kRowzStride] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -489,6 +508,7 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
     const int* __restrict__ depth, const int* __restrict__ n_nodes, float inv_t,
     uint64_t seed, uint64_t round, int max_depth, const float* __restrict__ cmax,
     const int* __restrict__ carg, const uint64_t* __restrict__ cz,
+    const float* __restrict__ rowm, const uint64_t* __restrict__ rowz,
     const uint64_t* __restrict__ wtg, const uint64_t* __restrict__ wqg, int64_t trows,
     int64_t rows, int* __restrict__ accept_len, int* __restrict__ accepted_nodes,
     int* __restrict__ out_tokens, DraftPending* __restrict__ pend) {
@@ -503,11 +523,12 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
 
   // ---- 1. every load that needs nothing but the shapes, issued together:
   // the tree and the children's weights (thread t owns nodes t + 256 k, all
-  // N rows are inside the arrays), the first batch of row statistics, and
-  // n_nodes.  Rows (all N of the sequence, then its K draft rows in DRAFT
-  // mode) are split into P parts of the chunk list so that every thread has
-  // work; lanes of a part hold consecutive rows, so each chunk-major load is
-  // coalesced.
+  // N rows are inside the arrays), the row statistics, and n_nodes.  Rows are
+  // all N of the sequence, then its K draft rows in DRAFT mode.  Sampled
+  // modes read each row's (maximum, mass) totals (thread t: rows t + 256 k).
+  // Greedy reads the chunk records: the rows are split into P parts of the
+  // chunk list so that every thread has work; lanes of a part hold
+  // consecutive rows, so each chunk-major load is coalesced.
   int pv[4], tv[4], dv[4];
   uint64_t wv[4], qv[4];
 #pragma unroll
@@ -542,7 +563,20 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
       else zv[q] = cz[at];
     }
   };
-  load_batch(0, part);
+  constexpr int kRowsPer = (kMaxN + kMaxDraftRows + kAccNT - 1) / kAccNT;
+  float tmv[kRowsPer];
+  uint64_t tzv[kRowsPer];
+  if constexpr (kSampled) {
+#pragma unroll
+    for (int k = 0; k < kRowsPer; ++k) {
+      const int r = tid + k * kAccNT;
+      const int64_t grow = r >= nr ? 0 : (r < N ? rb + r : trows + (int64_t)b * K + (r - N));
+      tmv[k] = rowm[grow];
+      tzv[k] = rowz[grow * kRowzStride];
+    }
+  } else {
+    load_batch(0, part);
+  }
   const int n = n_nodes[b];
   for (int j = tid; j < width; j += kAccNT) {
     acc_nodes[j] = -1;
@@ -573,7 +607,22 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
       }
     }
   };
-  for (int r0 = 0; r0 < nr; r0 += RP) {
+  if constexpr (kSampled) {
+    make_draws();  // while the row totals are in flight
+#pragma unroll
+    for (int k = 0; k < kRowsPer; ++k) {
+      const int rw = tid + k * kAccNT;
+      if (rw < N) {
+        sh.rmax[rw] = tmv[k];
+        sh.r.rz[rw] = tzv[k];
+      } else if (rw < nr) {
+        sh.dmax[rw - N] = tmv[k];
+        sh.dz[rw - N] = tzv[k];
+      }
+    }
+    __syncthreads();
+  }
+  for (int r0 = 0; r0 < (kSampled ? 0 : nr); r0 += RP) {
     const int r = r0 + rr;
     const bool act = part < P && r < nr;
     float m = -__builtin_inff();
@@ -595,7 +644,6 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
       }
     };
     if (r0 > 0) load_batch(r0, part);
-    if (kSampled && r0 == 0) make_draws();  // while the first loads are in flight
     if (act) {
       reduce_batch(part);
       for (int j0 = part + 16 * P; j0 < C; j0 += 16 * P) {
@@ -1011,6 +1059,8 @@ AcceptPlan accept_plan(int batch, int N, int K, int V, bool sampled, bool draft)
   p.off_pend = draft ? take((size_t)batch * sizeof(DraftPending)) : 0;
   p.slot_stride = (p.C + 31) & ~31;  // 256-byte rows of slots
   p.off_slot = sampled ? take((size_t)p.rows * p.slot_stride * sizeof(uint64_t)) : 0;
+  p.off_rowz = sampled ? take((size_t)p.rows * kRowzStride * sizeof(uint64_t)) : 0;
+  p.off_rowm = sampled ? take((size_t)p.rows * sizeof(float)) : 0;
   p.workspace = off;
   return p;
 }
@@ -1101,6 +1151,8 @@ static void launch_accept_t(const AcceptPlan& p, const T* target, const T* draft
   uint64_t* rcz = draft_proposal ? reinterpret_cast<uint64_t*>(w + p.off_rcz) : nullptr;
   DraftPending* pend =
       draft_proposal ? reinterpret_cast<DraftPending*>(w + p.off_pend) : nullptr;
+  uint64_t* rowz = sampled ? reinterpret_cast<uint64_t*>(w + p.off_rowz) : nullptr;
+  float* rowm = sampled ? reinterpret_cast<float*>(w + p.off_rowm) : nullptr;
   const int64_t trows = (int64_t)batch * N;
   const dim3 g(p.C, (unsigned)p.rows);
   const dim3 blk(kAccNT);
@@ -1109,12 +1161,12 @@ static void launch_accept_t(const AcceptPlan& p, const T* target, const T* draft
     const RowstatShape sh = rowstat_shape<T>(p.rows, V);
     hipLaunchKernelGGL(k_zero_slots,
                        dim3((unsigned)((p.rows * sh.Cb + kAccNT - 1) / kAccNT)), blk, 0, stream,
-                       slot, p.rows, sh.Cb, p.slot_stride);
+                       slot, p.rows, sh.Cb, p.slot_stride, rowz);
     const int spin = g_rowstat_spin_limit.load(std::memory_order_relaxed);
 #define TV_ROWSTAT(E, PIPE)                                                                    \
   hipLaunchKernelGGL((k_rowstat<T, E, PIPE>), dim3(sh.grid), blk, 0, stream, target, draft, V, \
-                     p.C, sh.Cb, trows, p.rows, inv_t, cmax, slot, p.slot_stride, cz, N, K,    \
-                     parent, token, depth, n_nodes, wtg, wqg, spin)
+                     p.C, sh.Cb, trows, p.rows, inv_t, cmax, slot, p.slot_stride, cz, rowm,    \
+                     rowz, N, K, parent, token, depth, n_nodes, wtg, wqg, spin)
     if (sh.E == 32)
       TV_ROWSTAT(32, false);
     else if (!sh.pipe)
@@ -1129,7 +1181,8 @@ static void launch_accept_t(const AcceptPlan& p, const T* target, const T* draft
 #define TV_WALK(M)                                                                            \
   hipLaunchKernelGGL((k_walk<T, M>), dim3(batch), blk, 0, stream, target, draft, N, K, V, p.C, \
                      parent, token, depth, n_nodes, inv_t, seed, round, max_depth, cmax, carg, \
-                     cz, wtg, wqg, trows, p.rows, accept_len, accepted_nodes, out_tokens, pend)
+                     cz, rowm, rowz, wtg, wqg, trows, p.rows, accept_len, accepted_nodes,     \
+                     out_tokens, pend)
   if (!sampled) {
     TV_WALK(kGreedy);
   } else if (!draft_proposal) {
