@@ -7,8 +7,9 @@
 //
 // Kernels (one stream, in order):
 //   k_chunk_topk   grid (chunks, b*K)  top-k of each 8192-token chunk of a draft row
-//   k_chunk_z      grid (chunks, b*K)  fixed-point softmax mass of each chunk
-//   k_finalize     grid (b*K)          row top-k, q = W / Z, rank by (q desc, id asc)
+//   k_chunk_z      grid (chunks, b*K)  fixed-point softmax mass of each chunk; the
+//                                      row's last block: row top-k, q = W / Z,
+//                                      rank by (q desc, id asc)
 //   k_select       grid (b)            exact best-B selection + rows + ancestors
 //
 // Selection (k_select).  Nodes are ordered by (score desc, depth asc,
@@ -43,16 +44,23 @@
 namespace tvk {
 
 constexpr int kBuildNT = 256;
+// per-row hand-off record of k_chunk_z (mass accumulator, arrival count),
+// one 256-byte line per row
+constexpr int kRowRec = 32;
 
 // ---------------------------------------------------------------------------
 template <typename T, int E>
 __global__ __launch_bounds__(kBuildNT) void k_chunk_topk(const T* __restrict__ logits, int V,
                                                         int C, int chunk, int k,
                                                         float* __restrict__ cval,
-                                                        int* __restrict__ cid) {
+                                                        int* __restrict__ cid,
+                                                        uint64_t* __restrict__ rowrec) {
   __shared__ TopkScratch<kBuildNT> sc;
   const int c = blockIdx.x;
   const int64_t row = blockIdx.y;
+  // the row's mass accumulator and arrival count for k_chunk_z, cleared
+  // here, one kernel ahead of their use
+  if (c == 0 && threadIdx.x < 2) rowrec[row * kRowRec + threadIdx.x] = 0;
   const T* p = logits + row * (int64_t)V;
   const int base = c * chunk;
   // A full chunk: thread t holds the E consecutive tokens [base + t*E, ...)
@@ -81,17 +89,59 @@ __global__ __launch_bounds__(kBuildNT) void k_chunk_topk(const T* __restrict__ l
 }
 
 // ---------------------------------------------------------------------------
+// A draft row's top-k from its chunks' candidates (val/id, padded with -inf
+// and ids >= V) and its mass Z: q = W / Z in fp64, written at rank order
+// (q desc, id asc) to ftok/fq[row][.].
+template <int E>
+__device__ __forceinline__ void finalize_candidates(float (&val)[E], int (&id)[E], uint64_t Z,
+                                                    int V, int k, float inv_t,
+                                                    TopkScratch<kBuildNT>& sc, float* tv,
+                                                    int* ti, double* tq, int* ftok, double* fq,
+                                                    int64_t row) {
+  block_topk<kBuildNT, E>(val, id, k, sc, tv, ti, V, V);  // ends with a barrier
+  const float m = tv[0];                                 // the row maximum
+  if ((int)threadIdx.x < k) {
+    uint64_t w = weight(tv[threadIdx.x], m, inv_t);
+    tq[threadIdx.x] = (double)w / (double)Z;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < k) {
+    const int t = threadIdx.x;
+    const double q = tq[t];
+    const int me = ti[t];
+    int r = 0;
+    for (int j = 0; j < k; ++j) r += (tq[j] > q || (tq[j] == q && ti[j] < me)) ? 1 : 0;
+    ftok[row * k + r] = me;
+    fq[row * k + r] = q;
+  }
+}
+
+// Fixed-point softmax mass of each chunk, and the row's finalisation by the
+// row's last block to finish.  The chunk's logits are loaded first; the row
+// maximum (over the chunk maxima, the first candidate of every chunk)
+// arrives while they are in flight.  Each block adds its mass into the row's
+// accumulator rowrec[row][0] (an integer atomic, so the order does not
+// matter) and, once that add is performed, counts itself in rowrec[row][1];
+// the block that counts last has the whole mass Z and finalises the row
+// from the chunks' candidates (written by k_chunk_topk, one kernel before).
+// The chunk masses also go to cz[row][c].
 template <typename T>
 __global__ __launch_bounds__(kBuildNT) void k_chunk_z(const T* __restrict__ logits, int V,
                                                      int C, int chunk, int k, float inv_t,
                                                      const float* __restrict__ cval,
-                                                     uint64_t* __restrict__ cz) {
+                                                     const int* __restrict__ cid,
+                                                     uint64_t* __restrict__ cz,
+                                                     uint64_t* rowrec, int* __restrict__ ftok,
+                                                     double* __restrict__ fq) {
+  __shared__ TopkScratch<kBuildNT> sc;
+  __shared__ float tv[TV_MAX_TOPK_];
+  __shared__ int ti[TV_MAX_TOPK_];
+  __shared__ double tq[TV_MAX_TOPK_];
   __shared__ uint64_t wsum[kBuildNT / WAVE];
   __shared__ float s_m;
+  __shared__ int s_last;
   const int c = blockIdx.x;
   const int64_t row = blockIdx.y;
-  // the chunk's logits first; the row maximum (over the chunk maxima, the
-  // first candidate of every chunk) arrives while they are in flight
   const T* p = logits + row * (int64_t)V;
   const int base = c * chunk;
   float x[kBuildChunk / kBuildNT];
@@ -115,57 +165,29 @@ __global__ __launch_bounds__(kBuildNT) void k_chunk_z(const T* __restrict__ logi
     uint64_t z = 0;
     for (int w = 0; w < kBuildNT / WAVE; ++w) z += wsum[w];
     cz[row * C + c] = z;
+    uint64_t* rec = rowrec + row * kRowRec;
+    (void)__hip_atomic_fetch_add(&rec[0], z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the add is performed before the count that announces it
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    s_last = __hip_atomic_fetch_add(&rec[1], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint64_t)(C - 1);
   }
-}
-
-// ---------------------------------------------------------------------------
-template <int E>
-__global__ __launch_bounds__(kBuildNT) void k_finalize(int V, int C, int chunk, int k,
-                                                      float inv_t,
-                                                      const float* __restrict__ cval,
-                                                      const int* __restrict__ cid,
-                                                      const uint64_t* __restrict__ cz,
-                                                      int* __restrict__ ftok,
-                                                      double* __restrict__ fq) {
-  __shared__ TopkScratch<kBuildNT> sc;
-  __shared__ float tv[TV_MAX_TOPK_];
-  __shared__ int ti[TV_MAX_TOPK_];
-  __shared__ double tq[TV_MAX_TOPK_];
-  __shared__ uint64_t s_z;
-  const int64_t row = blockIdx.x;
+  __syncthreads();
+  if (!s_last) return;
+  // the row's last block: the whole mass is in the accumulator
   const int n = C * k;
-  float val[E];
-  int id[E];
+  float val[kFinalizeE];
+  int id[kFinalizeE];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    int j = e * kBuildNT + (int)threadIdx.x;
-    bool ok = j < n;
+  for (int e = 0; e < kFinalizeE; ++e) {
+    const int j = e * kBuildNT + (int)threadIdx.x;
+    const bool ok = j < n;
     val[e] = ok ? cval[row * n + j] : -__builtin_inff();
     id[e] = ok ? cid[row * n + j] : V + C * chunk + j;
   }
-  if (threadIdx.x < WAVE) {
-    uint64_t z = 0;
-    for (int j = threadIdx.x; j < C; j += WAVE) z += cz[row * C + j];
-    z = wave_sum_u64(z);
-    if (threadIdx.x == 0) s_z = z;
-  }
-  block_topk<kBuildNT, E>(val, id, k, sc, tv, ti, V, V);  // ends with a barrier
-  const float m = tv[0];                             // the row maximum
-  const uint64_t Z = s_z;
-  if ((int)threadIdx.x < k) {
-    uint64_t w = weight(tv[threadIdx.x], m, inv_t);
-    tq[threadIdx.x] = (double)w / (double)Z;
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < k) {
-    const int t = threadIdx.x;
-    const double q = tq[t];
-    const int me = ti[t];
-    int r = 0;
-    for (int j = 0; j < k; ++j) r += (tq[j] > q || (tq[j] == q && ti[j] < me)) ? 1 : 0;
-    ftok[row * k + r] = me;
-    fq[row * k + r] = q;
-  }
+  const uint64_t Z =
+      __hip_atomic_load(&rowrec[row * kRowRec], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  finalize_candidates<kFinalizeE>(val, id, Z, V, k, inv_t, sc, tv, ti, tq, ftok, fq, row);
 }
 
 // ---------------------------------------------------------------------------
@@ -757,8 +779,27 @@ BuildPlan build_plan(int batch, int K, int V, int topk, int budget) {
   p.off_cz = take((size_t)p.rows * p.C * sizeof(uint64_t));
   p.off_ftok = take((size_t)p.rows * topk * sizeof(int));
   p.off_fq = take((size_t)p.rows * topk * sizeof(double));
+  p.off_rowrec = take((size_t)p.rows * kRowRec * sizeof(uint64_t));
   p.workspace = off;
   return p;
+}
+
+// Top-k, q = W / Z and ranks of p.rows logit rows into ftok/fq.
+template <typename T>
+static void launch_row_topk(const BuildPlan& p, const T* logits, int V, int k, float inv_t,
+                            char* w, hipStream_t stream) {
+  float* cval = reinterpret_cast<float*>(w + p.off_cval);
+  int* cid = reinterpret_cast<int*>(w + p.off_cid);
+  uint64_t* cz = reinterpret_cast<uint64_t*>(w + p.off_cz);
+  int* ftok = reinterpret_cast<int*>(w + p.off_ftok);
+  double* fq = reinterpret_cast<double*>(w + p.off_fq);
+  uint64_t* rowrec = reinterpret_cast<uint64_t*>(w + p.off_rowrec);
+  constexpr int E1 = kBuildChunk / kBuildNT;
+  const dim3 g1(p.C, (unsigned)p.rows);
+  hipLaunchKernelGGL((k_chunk_topk<T, E1>), g1, dim3(kBuildNT), 0, stream, logits, V, p.C,
+                     p.chunk, k, cval, cid, rowrec);
+  hipLaunchKernelGGL((k_chunk_z<T>), g1, dim3(kBuildNT), 0, stream, logits, V, p.C, p.chunk, k,
+                     inv_t, cval, cid, cz, rowrec, ftok, fq);
 }
 
 hipError_t launch_build(const BuildPlan& p, const void* draft, bool bf16, int batch, int K,
@@ -767,27 +808,12 @@ hipError_t launch_build(const BuildPlan& p, const void* draft, bool bf16, int ba
                         double* score, uint64_t* anc, int* n_nodes, void* ws,
                         hipStream_t stream) {
   char* w = static_cast<char*>(ws);
-  float* cval = reinterpret_cast<float*>(w + p.off_cval);
-  int* cid = reinterpret_cast<int*>(w + p.off_cid);
-  uint64_t* cz = reinterpret_cast<uint64_t*>(w + p.off_cz);
   int* ftok = reinterpret_cast<int*>(w + p.off_ftok);
   double* fq = reinterpret_cast<double*>(w + p.off_fq);
-  constexpr int E1 = kBuildChunk / kBuildNT;
-  dim3 g1(p.C, (unsigned)p.rows);
-  if (bf16) {
-    hipLaunchKernelGGL((k_chunk_topk<uint16_t, E1>), g1, dim3(kBuildNT), 0, stream,
-                       static_cast<const uint16_t*>(draft), V, p.C, p.chunk, topk, cval, cid);
-    hipLaunchKernelGGL((k_chunk_z<uint16_t>), g1, dim3(kBuildNT), 0, stream,
-                       static_cast<const uint16_t*>(draft), V, p.C, p.chunk, topk, inv_t, cval,
-                       cz);
-  } else {
-    hipLaunchKernelGGL((k_chunk_topk<float, E1>), g1, dim3(kBuildNT), 0, stream,
-                       static_cast<const float*>(draft), V, p.C, p.chunk, topk, cval, cid);
-    hipLaunchKernelGGL((k_chunk_z<float>), g1, dim3(kBuildNT), 0, stream,
-                       static_cast<const float*>(draft), V, p.C, p.chunk, topk, inv_t, cval, cz);
-  }
-  hipLaunchKernelGGL((k_finalize<kFinalizeE>), dim3((unsigned)p.rows), dim3(kBuildNT), 0,
-                     stream, V, p.C, p.chunk, topk, inv_t, cval, cid, cz, ftok, fq);
+  if (bf16)
+    launch_row_topk<uint16_t>(p, static_cast<const uint16_t*>(draft), V, topk, inv_t, w, stream);
+  else
+    launch_row_topk<float>(p, static_cast<const float*>(draft), V, topk, inv_t, w, stream);
   // one workgroup per sequence; larger budgets have longer candidate lists,
   // whose counting passes gain from more waves (measured: 256 threads up to
   // budget 127, 512 up to 511, then 1024)
@@ -821,29 +847,13 @@ hipError_t launch_tree_expand(const BuildPlan& p, const void* logits, bool bf16,
                               double* score, uint64_t* anc, int* n_nodes, int* next_frontier,
                               void* ws, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
-  float* cval = reinterpret_cast<float*>(w + p.off_cval);
-  int* cid = reinterpret_cast<int*>(w + p.off_cid);
-  uint64_t* cz = reinterpret_cast<uint64_t*>(w + p.off_cz);
   int* ftok = reinterpret_cast<int*>(w + p.off_ftok);
   double* fq = reinterpret_cast<double*>(w + p.off_fq);
-  constexpr int E1 = kBuildChunk / kBuildNT;
-  const dim3 g1(p.C, (unsigned)p.rows);
   // the frontier slots' rows take the place of the draft positions
-  if (bf16) {
-    const uint16_t* d = static_cast<const uint16_t*>(logits);
-    hipLaunchKernelGGL((k_chunk_topk<uint16_t, E1>), g1, dim3(kBuildNT), 0, stream, d, V, p.C,
-                       p.chunk, m, cval, cid);
-    hipLaunchKernelGGL((k_chunk_z<uint16_t>), g1, dim3(kBuildNT), 0, stream, d, V, p.C, p.chunk,
-                       m, inv_t, cval, cz);
-  } else {
-    const float* d = static_cast<const float*>(logits);
-    hipLaunchKernelGGL((k_chunk_topk<float, E1>), g1, dim3(kBuildNT), 0, stream, d, V, p.C,
-                       p.chunk, m, cval, cid);
-    hipLaunchKernelGGL((k_chunk_z<float>), g1, dim3(kBuildNT), 0, stream, d, V, p.C, p.chunk, m,
-                       inv_t, cval, cz);
-  }
-  hipLaunchKernelGGL((k_finalize<kFinalizeE>), dim3((unsigned)p.rows), dim3(kBuildNT), 0,
-                     stream, V, p.C, p.chunk, m, inv_t, cval, cid, cz, ftok, fq);
+  if (bf16)
+    launch_row_topk<uint16_t>(p, static_cast<const uint16_t*>(logits), V, m, inv_t, w, stream);
+  else
+    launch_row_topk<float>(p, static_cast<const float*>(logits), V, m, inv_t, w, stream);
   hipLaunchKernelGGL((k_expand<kBuildNT>), dim3(batch), dim3(kBuildNT), 0, stream, ftok, fq, W, m,
                      N, ctx_len, frontier, parent, token, depth, pos, score, anc, n_nodes,
                      next_frontier);

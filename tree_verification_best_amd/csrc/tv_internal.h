@@ -23,6 +23,7 @@ struct BuildPlan {
   int P;  // LDS room for the candidates of one depth (a power of two)
   size_t select_lds;
   size_t off_cval, off_cid, off_cz, off_ftok, off_fq;
+  size_t off_rowrec;  // per-row mass accumulator and arrival count (256-byte lines)
   size_t workspace;
 };
 
