@@ -181,9 +181,17 @@ __device__ __forceinline__ void chunk_mass(const float (&x)[E], const T* p, int 
   static_assert(E % 16 == 0 && E <= 512, "fp64 partial sums must stay exact");
   constexpr int kSpan = E * kAccNT;
   const int base = cb * kSpan;
-  double accd = (double)weight_f(x[0], m, inv_t);  // E weights of at most 2^44: exact
+  // E weights of at most 2^44 add exactly in fp64; -inf pads weigh 0
+  double accd;
+  if (inv_t == 1.0f) {
+    accd = (double)weight_f<true>(x[0], m, inv_t);
 #pragma unroll
-  for (int j = 1; j < E; ++j) accd += (double)weight_f(x[j], m, inv_t);  // -inf pads weigh 0
+    for (int j = 1; j < E; ++j) accd += (double)weight_f<true>(x[j], m, inv_t);
+  } else {
+    accd = (double)weight_f(x[0], m, inv_t);
+#pragma unroll
+    for (int j = 1; j < E; ++j) accd += (double)weight_f(x[j], m, inv_t);
+  }
   const uint64_t acc = wave_sum_u64((uint64_t)accd);
   if (lane_id() == 0) wsum[threadIdx.x / WAVE] = acc;
   if (wtg) {

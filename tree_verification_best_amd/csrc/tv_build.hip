@@ -155,9 +155,17 @@ __global__ __launch_bounds__(kBuildNT) void k_chunk_z(const T* __restrict__ logi
   __syncthreads();
   const float m = s_m;
   static_assert(kBuildChunk / kBuildNT <= 512, "fp64 partial sums must stay exact");
-  double accd = (double)weight_f(x[0], m, inv_t);
+  double accd;
+  if (inv_t == 1.0f) {
+    accd = (double)weight_f<true>(x[0], m, inv_t);
 #pragma unroll
-  for (int j = 1; j < kBuildChunk / kBuildNT; ++j) accd += (double)weight_f(x[j], m, inv_t);
+    for (int j = 1; j < kBuildChunk / kBuildNT; ++j)
+      accd += (double)weight_f<true>(x[j], m, inv_t);
+  } else {
+    accd = (double)weight_f(x[0], m, inv_t);
+#pragma unroll
+    for (int j = 1; j < kBuildChunk / kBuildNT; ++j) accd += (double)weight_f(x[j], m, inv_t);
+  }
   const uint64_t acc = wave_sum_u64((uint64_t)accd);
   if (lane_id() == 0) wsum[threadIdx.x / WAVE] = acc;
   __syncthreads();

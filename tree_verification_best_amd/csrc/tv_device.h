@@ -2,7 +2,7 @@
 // libtreeverify: the fixed-point softmax weight, Philox4x64-10, 64-lane
 // wavefront helpers and a block-wide top-k.
 //
-// Every translation unit that uses exp_spec / weight / Philox for an integer
+// Every translation unit that uses weight_f / weight / Philox for an integer
 // decision is compiled with -ffp-contract=off: each float operation below is
 // one IEEE operation in the order written.
 #pragma once
@@ -15,26 +15,50 @@ namespace tvk {
 constexpr int WAVE = 64;
 
 // ---------------------------------------------------------------------------
-// e^x for fp32 x <= 0 (0 below -32).  Cody-Waite reduction x = n ln2 + r with
-// n = rint(x * log2e) and ln2 split into a high part with 12 significand
-// bits (0x3f317000) and the fp32 rounding of the remainder (0x3805fdf4);
-// e^r from its Taylor series to degree 7 (coefficients fp32(1/i!)) by Horner
-// with fused multiply-adds; the result is scaled by 2^n exactly.  Written
-// without a branch: every lane evaluates the polynomial and the range test
-// selects the result (NaN and -inf inputs give 0).
+// Fixed-point weight of logit l in a row with maximum m at inverse
+// temperature inv_t: W = rint(exp32(x) * 2^44) for x = fl32(fl32(l - m) *
+// inv_t), where exp32 is e^x for fp32 x <= 0 and 0 below -32: Cody-Waite
+// reduction x = n ln2 + r with n = rint(x * log2e) and ln2 split into a high
+// part with 12 significand bits (0x3f317000) and the fp32 rounding of the
+// remainder (0x3805fdf4); e^r from its Taylor series to degree 7
+// (coefficients fp32(1/i!)) by Horner with fused multiply-adds; the result
+// scaled by 2^n exactly.
+//
+// The evaluation below gives the same W with fewer instructions:
+//   * x is clamped at -33 instead of tested against -32: every x below -32
+//     has W = 0 either way (e^-32 * 2^44 = 0.22 rounds to 0, and so does the
+//     polynomial's value), and NaN (an all -inf row) clamps to -33 as well;
+//   * n comes from adding 1.5 * 2^23 + 44 to x * log2e: the sum rounds to an
+//     integer (nearest even, as rint does; |x log2e| < 48), its difference
+//     with that constant is n exactly, and its low bits hold n + 44;
+//   * 2^n * 2^44 is applied by adding (n + 44) << 23 to the bits of the
+//     polynomial's value p in [0.70, 1.42]: the product stays a normal
+//     number (0.7 * 2^-4 and up), so this is the exact scaling; the 0x4B4
+//     exponent bits of the sum shift out of the 32-bit word.
+// UNIT = (inv_t == 1): x = l - m without the multiply (the same value).
+// weight_f returns W as an integer-valued float (exact: at most 2^44, and
+// fp32 holds every integer it rounds to); such integers also add exactly in
+// fp64 while a sum stays below 2^53, i.e. for up to 512 weights, which is
+// how the streaming kernels sum them before one conversion to uint64.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float exp_spec(float x) {
+template <bool UNIT = false>
+__device__ __forceinline__ float weight_f(float l, float m, float inv_t) {
   const float kLog2e = __builtin_bit_cast(float, 0x3fb8aa3bu);
   const float kLn2Hi = __builtin_bit_cast(float, 0x3f317000u);
   const float kLn2Lo = __builtin_bit_cast(float, 0x3805fdf4u);
+  const float kRound = 12582956.0f;  // 1.5 * 2^23 + 44
   const float c7 = __builtin_bit_cast(float, 0x39500d01u);
   const float c6 = __builtin_bit_cast(float, 0x3ab60b61u);
   const float c5 = __builtin_bit_cast(float, 0x3c088889u);
   const float c4 = __builtin_bit_cast(float, 0x3d2aaaabu);
   const float c3 = __builtin_bit_cast(float, 0x3e2aaaabu);
   const float c2 = 0.5f;
-  float t = x * kLog2e;
-  float n = __builtin_rintf(t);
+  const float d = l - m;
+  float x = UNIT ? d : d * inv_t;
+  x = __builtin_fmaxf(x, -33.0f);
+  const float t = x * kLog2e;
+  const float f = t + kRound;  // kRound + rint(t)
+  const float n = f - kRound;  // rint(t), exact
   float r = __builtin_fmaf(-n, kLn2Hi, x);
   r = __builtin_fmaf(-n, kLn2Lo, r);
   float p = c7;
@@ -45,22 +69,9 @@ __device__ __forceinline__ float exp_spec(float x) {
   p = __builtin_fmaf(p, r, c2);
   p = __builtin_fmaf(p, r, 1.0f);
   p = __builtin_fmaf(p, r, 1.0f);
-  const float e = __builtin_ldexpf(p, (int)n);
-  return x >= -32.0f ? e : 0.0f;
-}
-
-// Fixed-point weight of logit l in a row with maximum m at inverse
-// temperature inv_t: rint(exp_spec(fl32(fl32(l - m) * inv_t)) * 2^44).
-// weight_f returns it as an integer-valued float (exact: at most 2^44, and
-// fp32 holds every integer it rounds to); such integers also add exactly in
-// fp64 while a sum stays below 2^53, i.e. for up to 512 weights, which is
-// how the streaming kernels sum them before one conversion to uint64.
-__device__ __forceinline__ float weight_f(float l, float m, float inv_t) {
-  float d = l - m;
-  float x = d * inv_t;
-  float e = exp_spec(x);
-  float s = e * 17592186044416.0f;  // 2^44
-  return __builtin_rintf(s);
+  const uint32_t s =
+      __builtin_bit_cast(uint32_t, p) + (__builtin_bit_cast(uint32_t, f) << 23);  // p 2^(n+44)
+  return __builtin_rintf(__builtin_bit_cast(float, s));
 }
 
 __device__ __forceinline__ uint64_t weight(float l, float m, float inv_t) {
