@@ -41,7 +41,6 @@
 namespace tvk {
 
 constexpr int kAccNT = 256;
-constexpr int kAccE = kAcceptChunk / kAccNT;  // 16 tokens per thread and chunk
 constexpr int kMaxN = 1024;                   // rows per sequence
 constexpr int kMaxDraftRows = 64;             // drafter positions (DRAFT proposal)
 constexpr int kMaxChunks = 64;                // chunks per row (V <= 2^18)
@@ -553,22 +552,22 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
   const int P = min(C, max(1, kAccNT / nr));
   const int RP = kAccNT / P;
   const int part = tid / RP, rr = tid - part * RP;
-  float mv[16];
-  int av[16];
-  uint64_t zv[16];
-  // a batch of 16 chunks of row pass r0 (addresses clamped inside the arrays
-  // for idle threads and past the last chunk)
+  // greedy: a batch of kGB chunks of row pass r0 (addresses clamped inside
+  // the arrays for idle threads and past the last chunk).  Batches of 48
+  // (one per pass at 151936 tokens) measured the same as batches of 16.
+  constexpr int kGB = kSampled ? 1 : 16;
+  float mv[kGB];
+  int av[kGB];
   auto load_batch = [&](int r0, int j0) {
     const int r = r0 + rr;
     const bool act = part < P && r < nr;
     const int64_t grow = !act ? 0 : (r < N ? rb + r : trows + (int64_t)b * K + (r - N));
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < kGB; ++q) {
       const int j = j0 + q * P;
       const int64_t at = (int64_t)(j < C ? j : 0) * rows + grow;
       mv[q] = cmax[at];
-      if (!kSampled) av[q] = carg[at];
-      else zv[q] = cz[at];
+      av[q] = carg[at];
     }
   };
   constexpr int kRowsPer = (kMaxN + kMaxDraftRows + kAccNT - 1) / kAccNT;
@@ -635,26 +634,20 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
     const bool act = part < P && r < nr;
     float m = -__builtin_inff();
     int a = 0x7fffffff;
-    uint64_t z = 0;
     auto reduce_batch = [&](int j0) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
+      for (int q = 0; q < kGB; ++q) {
         const bool in = j0 + q * P < C;  // no early exit: the loads stay batched
-        if (!kSampled) {
-          if (in && vi_better(mv[q], av[q], m, a)) {
-            m = mv[q];
-            a = av[q];
-          }
-        } else {
-          m = fmaxf(m, in ? mv[q] : -__builtin_inff());
-          z += in ? zv[q] : 0ull;
+        if (in && vi_better(mv[q], av[q], m, a)) {
+          m = mv[q];
+          a = av[q];
         }
       }
     };
     if (r0 > 0) load_batch(r0, part);
     if (act) {
       reduce_batch(part);
-      for (int j0 = part + 16 * P; j0 < C; j0 += 16 * P) {
+      for (int j0 = part + kGB * P; j0 < C; j0 += kGB * P) {
         load_batch(r0, j0);
         reduce_batch(j0);
       }
@@ -662,34 +655,21 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
     if (part < P) {
       sh.pmax[tid] = m;
       sh.parg[tid] = a;
-      sh.pz[tid] = z;
     }
     __syncthreads();
     if (tid < RP && r0 + tid < nr) {
       const int rw = r0 + tid;
       float bm = sh.pmax[tid];
       int ba = sh.parg[tid];
-      uint64_t bz = sh.pz[tid];
       for (int q = 1; q < P; ++q) {
         const int i = q * RP + tid;
-        if (!kSampled) {
-          if (vi_better(sh.pmax[i], sh.parg[i], bm, ba)) {
-            bm = sh.pmax[i];
-            ba = sh.parg[i];
-          }
-        } else {
-          bm = fmaxf(bm, sh.pmax[i]);
-          bz += sh.pz[i];
+        if (vi_better(sh.pmax[i], sh.parg[i], bm, ba)) {
+          bm = sh.pmax[i];
+          ba = sh.parg[i];
         }
       }
-      if (rw < N) {
-        sh.rmax[rw] = bm;
-        if (!kSampled) sh.r.rarg[rw] = ba;
-        else sh.r.rz[rw] = bz;
-      } else {
-        sh.dmax[rw - N] = bm;
-        sh.dz[rw - N] = bz;
-      }
+      sh.rmax[rw] = bm;  // greedy has no draft rows: rw < N
+      sh.r.rarg[rw] = ba;
     }
     __syncthreads();
   }
