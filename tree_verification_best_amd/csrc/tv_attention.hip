@@ -494,23 +494,24 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
 
 // Merge the S + 1 partials of every query row.  Partial s holds O_s / l_s in
 // fp16; its weight is 2^(m_s - M) l_s / L with L = sum_s 2^(m_s - M) l_s.
-// One thread per (row, head, 4 output columns): the D/4 threads of a row
+// One thread per (row, head, 8 output columns): the D/8 threads of a row
 // read the same (m_s, l_s) words.  Up to kOne = 16 partials are loaded in one
 // round (with the sequence's node count alongside; rows past it are written
 // as zeros), so the kernel waits on memory once; more splits take batches of
 // eight, with the maximum found first.  The sum runs over s in order either
 // way.
-template <typename OutT>
-__device__ __forceinline__ void combine_add(float m, float l, uint2 h, float M, float& lsum,
-                                            float4& acc) {
+__device__ __forceinline__ void combine_add(float m, float l, uint4 h, float M, float& lsum,
+                                            float (&acc)[8]) {
   const bool live = m != -__builtin_inff();
   const float wgt = live ? __builtin_amdgcn_exp2f(m - M) : 0.f;
   const float wl = wgt * l;  // the partial holds O / l
   lsum += wl;
-  acc.x += wl * (float)__builtin_bit_cast(_Float16, (uint16_t)(h.x & 0xFFFFu));
-  acc.y += wl * (float)__builtin_bit_cast(_Float16, (uint16_t)(h.x >> 16));
-  acc.z += wl * (float)__builtin_bit_cast(_Float16, (uint16_t)(h.y & 0xFFFFu));
-  acc.w += wl * (float)__builtin_bit_cast(_Float16, (uint16_t)(h.y >> 16));
+  const uint32_t w[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] += wl * (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xFFFFu));
+    acc[2 * i + 1] += wl * (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+  }
 }
 
 template <typename OutT>
@@ -523,32 +524,34 @@ __global__ __launch_bounds__(256) void k_attn_combine(const uint16_t* __restrict
                                                      float* __restrict__ lse) {
   constexpr int kOne = 16;  // partials loaded in one round
   constexpr int kB = 8;     // splits per load batch beyond that
-  const int D4 = D / 4;
+  const int D8 = D / 8;
   const int64_t plane = (int64_t)batch * N * Hq;
-  const int64_t r = (int64_t)blockIdx.x * (256 / D4) + threadIdx.x / D4;  // (b, node, head)
+  const int64_t r = (int64_t)blockIdx.x * (256 / D8) + threadIdx.x / D8;  // (b, node, head)
   if (r >= plane) return;
-  const int d4 = threadIdx.x % D4;
+  const int d8 = threadIdx.x % D8;
   const int64_t bn = r / Hq;
   const int b = (int)(bn / N), node = (int)(bn % N);
-  OutT* dst = out + r * D + 4 * d4;
-  const uint16_t* ob = Opart + r * D + 4 * d4;
+  OutT* dst = out + r * D + 8 * d8;
+  const uint16_t* ob = Opart + r * D + 8 * d8;
   const int nb = n_nodes[b];
   float M = -__builtin_inff();
   float lsum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   if (S1 <= kOne) {
     float ms[kOne], ls[kOne];
-    uint2 oh[kOne];
+    uint4 oh[kOne];
 #pragma unroll
     for (int j = 0; j < kOne; ++j) {
       if (j < S1) {  // uniform
         ms[j] = Mpart[j * plane + r];
         ls[j] = Lpart[j * plane + r];
-        oh[j] = *reinterpret_cast<const uint2*>(ob + j * plane * D);
+        oh[j] = *reinterpret_cast<const uint4*>(ob + j * plane * D);
       } else {
         ms[j] = -__builtin_inff();
         ls[j] = 0.f;
-        oh[j] = make_uint2(0u, 0u);
+        oh[j] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
     if (node >= min(nb, N)) goto pad;
@@ -557,7 +560,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(const uint16_t* __restrict
       if (j < S1) M = fmaxf(M, ms[j]);
 #pragma unroll
     for (int j = 0; j < kOne; ++j)
-      if (j < S1) combine_add<OutT>(ms[j], ls[j], oh[j], M, lsum, acc);
+      if (j < S1) combine_add(ms[j], ls[j], oh[j], M, lsum, acc);
   } else {
     if (node >= min(nb, N)) goto pad;
     for (int s0 = 0; s0 < S1; s0 += kB) {
@@ -570,42 +573,46 @@ __global__ __launch_bounds__(256) void k_attn_combine(const uint16_t* __restrict
     }
     for (int s0 = 0; s0 < S1; s0 += kB) {
       float ms[kB], ls[kB];
-      uint2 oh[kB];
+      uint4 oh[kB];
 #pragma unroll
       for (int j = 0; j < kB; ++j) {
         const int s = min(s0 + j, S1 - 1);
         ms[j] = Mpart[s * plane + r];
         ls[j] = Lpart[s * plane + r];
-        oh[j] = *reinterpret_cast<const uint2*>(ob + s * plane * D);
+        oh[j] = *reinterpret_cast<const uint4*>(ob + s * plane * D);
       }
 #pragma unroll
       for (int j = 0; j < kB; ++j)
-        if (s0 + j < S1) combine_add<OutT>(ms[j], ls[j], oh[j], M, lsum, acc);
+        if (s0 + j < S1) combine_add(ms[j], ls[j], oh[j], M, lsum, acc);
     }
   }
   {
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    acc.x *= inv;
-    acc.y *= inv;
-    acc.z *= inv;
-    acc.w *= inv;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= inv;
     if constexpr (sizeof(OutT) == 2) {
-      *reinterpret_cast<uint2*>(dst) = make_uint2(
-          (uint32_t)f32_to_bf16_bits(acc.x) | ((uint32_t)f32_to_bf16_bits(acc.y) << 16),
-          (uint32_t)f32_to_bf16_bits(acc.z) | ((uint32_t)f32_to_bf16_bits(acc.w) << 16));
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)f32_to_bf16_bits(acc[2 * i]) |
+               ((uint32_t)f32_to_bf16_bits(acc[2 * i + 1]) << 16);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
     } else {
-      *reinterpret_cast<float4*>(dst) = acc;
+      reinterpret_cast<float4*>(dst)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      reinterpret_cast<float4*>(dst)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
     }
-    if (lse && d4 == 0)
+    if (lse && d8 == 0)
       lse[r] = lsum > 0.f ? (M + log2f(lsum)) * 0.69314718055994531f : -__builtin_inff();
     return;
   }
 pad:
-  if constexpr (sizeof(OutT) == 2)
-    *reinterpret_cast<uint2*>(dst) = make_uint2(0u, 0u);
-  else
-    *reinterpret_cast<float4*>(dst) = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (lse && d4 == 0) lse[r] = -__builtin_inff();
+  if constexpr (sizeof(OutT) == 2) {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    reinterpret_cast<float4*>(dst)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+    reinterpret_cast<float4*>(dst)[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (lse && d8 == 0) lse[r] = -__builtin_inff();
 }
 
 // ---------------------------------------------------------------------------
@@ -816,7 +823,7 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, con
       TV_PARTIAL(64, false);
   }
 #undef TV_PARTIAL
-  const unsigned cgrid = (unsigned)((rows + (256 / (D / 4)) - 1) / (256 / (D / 4)));
+  const unsigned cgrid = (unsigned)((rows + (256 / (D / 8)) - 1) / (256 / (D / 8)));
   if (out_f32)
     hipLaunchKernelGGL((k_attn_combine<float>), dim3(cgrid), dim3(256), 0, stream, Opart, Mpart,
                        Lpart, n_nodes, batch, N, Hq, D, p.splits + 1, static_cast<float*>(out),
