@@ -11,6 +11,7 @@
  *   tv_tree_ancestors, tv_tree_check   trees that come from elsewhere
  *   tv_tree_root, tv_tree_expand       a layer-wise builder (root, then one
  *                                      call per drafting step)
+ *   tv_tree_build_noalloc              tv_tree_build without a workspace
  *   tv_tree_budget                     cost-aware tree size
  *   tv_kv_commit                       keep the accepted path in the KV cache
  *   tv_tree_attention_verify_rope, tv_kv_commit_rope
@@ -21,10 +22,13 @@
  *   - Every array argument is a DEVICE pointer owned by the caller, dense
  *     and row-major in the layout given in its comment.  The library
  *     allocates and frees nothing; scratch space is the caller's
- *     `workspace` of at least the size the matching *_workspace() returns.
+ *     `workspace` of at least the size the matching *_workspace() returns
+ *     (tv_tree_build_noalloc uses a static buffer of the library instead).
  *   - Calls are asynchronous on `stream`: they enqueue kernels and return
  *     without synchronising.  The library keeps no global mutable state, so
- *     calls from several host threads on different streams are safe (for
+ *     calls from several host threads on different streams are safe
+ *     (except overlapping tv_tree_build_noalloc calls on one GPU, which
+ *     share that GPU's scratch buffer; for
  *     large budgets tv_tree_build raises its selection kernel's dynamic-LDS
  *     limit in the HIP runtime, an idempotent setting; the test hook
  *     tv_debug_set_spin_limit changes a process-wide setting).
@@ -80,6 +84,8 @@ typedef enum { TV_PROPOSAL_POINT_MASS = 0, TV_PROPOSAL_DRAFT = 1 } tv_proposal;
 #define TV_MAX_TOPK 64
 #define TV_MAX_BUDGET 1023
 #define TV_MAX_POSITIONS 64
+/* Size of the static device scratch behind tv_tree_build_noalloc. */
+#define TV_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
 
 /* Human-readable name of a status code (static storage). */
 const char *tv_status_string(tv_status s);
@@ -141,6 +147,29 @@ tv_status tv_tree_build(const void *draft_logits, tv_dtype dt, int batch, int K,
                         int32_t *depth, int32_t *pos, double *score, uint64_t *anc_mask,
                         int32_t *n_nodes, void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * tv_tree_build_noalloc -- tv_tree_build for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc.  Same arguments (less the workspace), results,
+ * limits and status codes as tv_tree_build.
+ *
+ * The workspace is a static device buffer of TV_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends.  A shape
+ * whose tv_tree_build_workspace() exceeds it returns TV_ERR_UNSUPPORTED
+ * before any device call.  The first call on a device looks up that device's
+ * copy of the buffer (hipGetSymbolAddress; TV_ERR_DEVICE if that fails); no
+ * call allocates or frees.  Every call on one GPU uses the same buffer and
+ * leaves its contents behind (the kernels set what they read first), so
+ * calls whose execution overlaps on one GPU -- from different streams or
+ * host threads -- race; the caller orders them.
+ * ------------------------------------------------------------------------ */
+tv_status tv_tree_build_noalloc(const void *draft_logits, tv_dtype dt, int batch, int K, int V,
+                                int topk, int budget, float build_temp,
+                                const int32_t *root_token, const int32_t *ctx_len,
+                                int32_t *parent, int32_t *token, int32_t *depth, int32_t *pos,
+                                double *score, uint64_t *anc_mask, int32_t *n_nodes,
+                                hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * tv_tree_ancestors -- depth, position ids and ancestor bit rows of trees

@@ -20,7 +20,7 @@ def _declared():
 
 def test_header_functions_exported():
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 19
     lib = ctypes.CDLL(tv.LIBPATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -88,6 +88,42 @@ def _build(**kw):
 ])
 def test_build_rejects(kw, status):
     assert _build(**kw) == status
+
+
+def _build_noalloc(**kw):
+    a = dict(draft=FAKE, dt=0, batch=1, K=4, V=100, topk=4, budget=8, temp=1.0, root=FAKE,
+             ctx=FAKE, parent=FAKE, token=FAKE, depth=FAKE, pos=FAKE, score=FAKE, anc=FAKE,
+             n=FAKE)
+    a.update(kw)
+    return tv.lib().tv_tree_build_noalloc(a["draft"], a["dt"], a["batch"], a["K"], a["V"],
+                                          a["topk"], a["budget"], a["temp"], a["root"],
+                                          a["ctx"], a["parent"], a["token"], a["depth"],
+                                          a["pos"], a["score"], a["anc"], a["n"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(draft=None), tv.TV_ERR_INVALID),
+    (dict(anc=None), tv.TV_ERR_INVALID),
+    (dict(temp=-1.0), tv.TV_ERR_INVALID),
+    (dict(K=65), tv.TV_ERR_UNSUPPORTED),
+    (dict(budget=1024), tv.TV_ERR_UNSUPPORTED),
+    # the shape's workspace exceeds the static scratch: refused before any device call
+    (dict(batch=512, K=16, V=151936, topk=16, budget=64), tv.TV_ERR_UNSUPPORTED),
+])
+def test_build_noalloc_rejects(kw, status):
+    assert _build_noalloc(**kw) == status
+
+
+def test_build_noalloc_limit_matches_workspace():
+    """Shapes up to the scratch size pass the size check; the first beyond it fails."""
+    L = tv.lib()
+    cap = 4 << 20
+    fits = [b for b in range(1, 200) if L.tv_tree_build_workspace(b, 16, 151936, 16, 64) <= cap]
+    assert fits and fits[-1] < 199
+    over = fits[-1] + 1
+    assert L.tv_tree_build_workspace(over, 16, 151936, 16, 64) > cap
+    assert _build_noalloc(batch=over, K=16, V=151936, topk=16, budget=64) == \
+        tv.TV_ERR_UNSUPPORTED
 
 
 def _attn(**kw):

@@ -40,7 +40,7 @@ EXPORTS = ("tv_status_string", "tv_version", "tv_tree_build_workspace", "tv_tree
            "tv_tree_accept_workspace", "tv_tree_accept", "tv_tree_budget", "tv_kv_commit",
            "tv_tree_root", "tv_tree_expand_workspace", "tv_tree_expand",
            "tv_tree_attention_verify_rope", "tv_kv_commit_rope", "tv_tree_check",
-           "tv_debug_set_spin_limit")
+           "tv_debug_set_spin_limit", "tv_tree_build_noalloc")
 
 _lib = None
 
@@ -73,6 +73,9 @@ def _load():
     L.tv_tree_build.argtypes = [vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp,
                                 vp, vp, vp, vp, sz, vp]
     L.tv_tree_build.restype = i32
+    L.tv_tree_build_noalloc.argtypes = [vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp,
+                                        vp, vp, vp, vp, vp]
+    L.tv_tree_build_noalloc.restype = i32
     L.tv_tree_ancestors.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp]
     L.tv_tree_ancestors.restype = i32
     L.tv_tree_attention_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i32]
@@ -161,21 +164,24 @@ def tree_build_workspace(batch, K, V, topk, budget):
     return _load().tv_tree_build_workspace(batch, K, V, topk, budget)
 
 
+def _tree_out(b, N, dev):
+    W = (N + 63) // 64
+    i32 = dict(dtype=torch.int32, device=dev)
+    return dict(parent=torch.empty((b, N), **i32), token=torch.empty((b, N), **i32),
+                depth=torch.empty((b, N), **i32), pos=torch.empty((b, N), **i32),
+                score=torch.empty((b, N), dtype=torch.float64, device=dev),
+                anc=torch.empty((b, N, W), dtype=torch.int64, device=dev),
+                n_nodes=torch.empty((b,), **i32))
+
+
 def tv_tree_build(draft_logits, topk, budget, root_token, ctx_len, build_temp=1.0,
                   workspace=None, out=None):
     """draft_logits [b][K][V] (f32/bf16) -> dict of tree tensors [b][budget+1]."""
     L = _load()
     b, K, V = draft_logits.shape
     dev = draft_logits.device
-    N = budget + 1
-    W = (N + 63) // 64
     if out is None:
-        i32 = dict(dtype=torch.int32, device=dev)
-        out = dict(parent=torch.empty((b, N), **i32), token=torch.empty((b, N), **i32),
-                   depth=torch.empty((b, N), **i32), pos=torch.empty((b, N), **i32),
-                   score=torch.empty((b, N), dtype=torch.float64, device=dev),
-                   anc=torch.empty((b, N, W), dtype=torch.int64, device=dev),
-                   n_nodes=torch.empty((b,), **i32))
+        out = _tree_out(b, budget + 1, dev)
     need = L.tv_tree_build_workspace(b, K, V, topk, budget)
     ws, wsb = _workspace(need, dev, workspace)
     st = L.tv_tree_build(_dev(draft_logits, "draft_logits"), _dt(draft_logits), b, K, V, topk,
@@ -186,6 +192,26 @@ def tv_tree_build(draft_logits, topk, budget, root_token, ctx_len, build_temp=1.
                          _dev(out["anc"], "anc"), _dev(out["n_nodes"], "n_nodes"),
                          ws.data_ptr(), wsb, _stream(dev))
     _check(st, "tv_tree_build")
+    return out
+
+
+def tv_tree_build_noalloc(draft_logits, topk, budget, root_token, ctx_len, build_temp=1.0,
+                          out=None):
+    """tv_tree_build on the library's static scratch: no workspace argument
+    and no device allocation when `out` is given."""
+    L = _load()
+    b, K, V = draft_logits.shape
+    if out is None:
+        out = _tree_out(b, budget + 1, draft_logits.device)
+    st = L.tv_tree_build_noalloc(_dev(draft_logits, "draft_logits"), _dt(draft_logits), b, K, V,
+                                 topk, budget, float(build_temp),
+                                 _dev(root_token, "root_token", torch.int32),
+                                 _dev(ctx_len, "ctx_len", torch.int32),
+                                 _dev(out["parent"], "parent"), _dev(out["token"], "token"),
+                                 _dev(out["depth"], "depth"), _dev(out["pos"], "pos"),
+                                 _dev(out["score"], "score"), _dev(out["anc"], "anc"),
+                                 _dev(out["n_nodes"], "n_nodes"), _stream(draft_logits.device))
+    _check(st, "tv_tree_build_noalloc")
     return out
 
 

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "tv_internal.h"
 #include "treeverify.h"
@@ -35,6 +36,59 @@ bool accept_args_ok(int batch, int N, int V, int max_depth) {
 
 tv_status device_status(hipError_t e) { return e == hipSuccess ? TV_OK : TV_ERR_DEVICE; }
 
+// Checks of tv_tree_build's arguments that need no workspace; fills the plan.
+tv_status build_check(const void* draft_logits, tv_dtype dt, int batch, int K, int V, int topk,
+                      int budget, float build_temp, const int32_t* root_token,
+                      const int32_t* ctx_len, const int32_t* parent, const int32_t* token,
+                      const int32_t* depth, const int32_t* pos, const double* score,
+                      const uint64_t* anc_mask, const int32_t* n_nodes, tvk::BuildPlan* plan) {
+  if (!draft_logits || !root_token || !ctx_len || !parent || !token || !depth || !pos ||
+      !score || !anc_mask || !n_nodes)
+    return TV_ERR_INVALID;
+  if (dt != TV_F32 && dt != TV_BF16) return TV_ERR_INVALID;
+  if (!finite_pos(build_temp)) return TV_ERR_INVALID;
+  if (batch < 1 || K < 1 || V < 1 || topk < 1 || topk > V || budget < 0) return TV_ERR_INVALID;
+  if (!build_args_ok(batch, K, V, topk, budget)) return TV_ERR_UNSUPPORTED;
+  *plan = tvk::build_plan(batch, K, V, topk, budget);
+  if (plan->C * topk > 256 * tvk::kFinalizeE || plan->select_lds > kMaxSelectLds ||
+      plan->rows > kMaxGridY)
+    return TV_ERR_UNSUPPORTED;
+  return TV_OK;
+}
+
+}  // namespace
+
+// Scratch of tv_tree_build_noalloc: a file-scope device array, one copy per
+// GPU, zero at load and held until the process ends.  In host code its name
+// is a host-side stand-in, not a device address: the address of a device's
+// copy comes from hipGetSymbolAddress, looked up once per device with that
+// device current, and only that address is passed on.
+static __device__ __align__(256) unsigned char scratch[TV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`.
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -64,22 +118,36 @@ tv_status tv_tree_build(const void* draft_logits, tv_dtype dt, int batch, int K,
                         int32_t* depth, int32_t* pos, double* score, uint64_t* anc_mask,
                         int32_t* n_nodes, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {
-  if (!draft_logits || !root_token || !ctx_len || !parent || !token || !depth || !pos ||
-      !score || !anc_mask || !n_nodes)
-    return TV_ERR_INVALID;
-  if (dt != TV_F32 && dt != TV_BF16) return TV_ERR_INVALID;
-  if (!finite_pos(build_temp)) return TV_ERR_INVALID;
-  if (batch < 1 || K < 1 || V < 1 || topk < 1 || topk > V || budget < 0) return TV_ERR_INVALID;
-  if (!build_args_ok(batch, K, V, topk, budget)) return TV_ERR_UNSUPPORTED;
-  const tvk::BuildPlan p = tvk::build_plan(batch, K, V, topk, budget);
-  if (p.C * topk > 256 * tvk::kFinalizeE || p.select_lds > kMaxSelectLds ||
-      p.rows > kMaxGridY)
-    return TV_ERR_UNSUPPORTED;
+  tvk::BuildPlan p{};
+  const tv_status st = build_check(draft_logits, dt, batch, K, V, topk, budget, build_temp,
+                                   root_token, ctx_len, parent, token, depth, pos, score,
+                                   anc_mask, n_nodes, &p);
+  if (st != TV_OK) return st;
   if (!workspace || workspace_bytes < p.workspace) return TV_ERR_WORKSPACE;
-  const float inv_t = 1.0f / build_temp;
   return device_status(tvk::launch_build(p, draft_logits, dt == TV_BF16, batch, K, V, topk,
-                                         budget, inv_t, root_token, ctx_len, parent, token,
-                                         depth, pos, score, anc_mask, n_nodes, workspace,
+                                         budget, 1.0f / build_temp, root_token, ctx_len, parent,
+                                         token, depth, pos, score, anc_mask, n_nodes, workspace,
+                                         stream));
+}
+
+tv_status tv_tree_build_noalloc(const void* draft_logits, tv_dtype dt, int batch, int K, int V,
+                                int topk, int budget, float build_temp,
+                                const int32_t* root_token, const int32_t* ctx_len,
+                                int32_t* parent, int32_t* token, int32_t* depth, int32_t* pos,
+                                double* score, uint64_t* anc_mask, int32_t* n_nodes,
+                                hipStream_t stream) {
+  tvk::BuildPlan p{};
+  const tv_status st = build_check(draft_logits, dt, batch, K, V, topk, budget, build_temp,
+                                   root_token, ctx_len, parent, token, depth, pos, score,
+                                   anc_mask, n_nodes, &p);
+  if (st != TV_OK) return st;
+  if (p.workspace > TV_NOALLOC_SCRATCH_BYTES) return TV_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return TV_ERR_DEVICE;
+  return device_status(tvk::launch_build(p, draft_logits, dt == TV_BF16, batch, K, V, topk,
+                                         budget, 1.0f / build_temp, root_token, ctx_len, parent,
+                                         token, depth, pos, score, anc_mask, n_nodes, ws,
                                          stream));
 }
 
