@@ -17,7 +17,7 @@ timed per call after the steps and reported as per_call.attention_rope.
 config.b_sweep_ms is the verification time against the tree budget B (one
 sequence, context 4096, B = 16 .. 512), the measured cost that the timed
 tv_tree_budget call takes as its cost curve.  config.cpu_all_cores repeats
-the CPU baseline with the BLAS pool on every usable host core (at most 16).
+the CPU baseline spread over the usable host cores (at most 16).
 The default workload is the 4B-class GQA layer (32 query / 8 KV heads, head
 dim 128, bf16, context 4096, K = 16 draft positions, top-8, budget 64,
 vocabulary 151936, sampled acceptance at T = 1).  Inputs rotate over enough
@@ -25,13 +25,20 @@ independent sets (>= 1 GiB) that every step reads HBM, not the 256 MB
 Infinity Cache.
 
 Prints ONE JSON line (rank 0).  `value` = tree node x query-head rows
-verified per second (rounds/s x N x Hq).  `roofline` is for the verification
-pass, tv_tree_attention_verify (kernels k_attn_partial + k_attn_combine),
-from HIP events recorded around every call on the stream the call runs on;
-its `traffic` comes from the HBM byte counters recorded in
+verified per second (rounds/s x N x Hq); config.batch_ms splits the timed
+steps into five equal batches (median beside the mean).  `roofline` is for
+the dominant kernel of the verification pass, k_attn_partial: its
+algorithmic bytes (every input of the call read once) or the call's flops
+over its own duration, from HIP events on the call's stream -- one recorded
+before the call and one that the library records between the partial and
+combine kernels (its timing hook) -- with the whole call's figures in
+roofline.call.  Its `traffic` comes from the HBM byte counters recorded in
 profiles/attention_<workload>_traffic.md when that record was taken on the
-current attention source (else null).  `cpu_baseline` times the CPU oracle
-on a bounded sample of the same workload.
+current attention source (else null).  per_call.attention_8b is the
+verification call at the 256-node shape (8B-class layer), timed the same
+way after the steps.  mean_accept_len is the mean accept length over every
+timed eager step (summed on the device).  `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 500] [--warmup 50] [--workload 4b] [--eager]
     python bench.py --copy-calibration      # a plain device copy of known size,
@@ -94,8 +101,9 @@ def source_digest(path):
 
 
 def recorded_traffic(workload):
-    """HBM bytes per tv_tree_attention_verify call from the committed counter
-    record, if it was taken on the current attention source."""
+    """HBM bytes per launch of k_attn_partial (FETCH_SIZE + WRITE_SIZE, each
+    scaled by the copy calibration) from the committed counter record, if it
+    was taken on the current attention source."""
     rec = os.path.join(ROOT, "profiles", f"attention_{workload}_traffic.md")
     src = os.path.join(ROOT, "tree_verification_best_amd", "csrc", "tv_attention.hip")
     if not os.path.exists(rec):
@@ -108,7 +116,7 @@ def recorded_traffic(workload):
     if vals.get("source_sha256_16") != source_digest(src):
         return None
     try:
-        return int(vals["hbm_bytes_per_call"])
+        return int(vals["k_attn_partial_hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -146,20 +154,32 @@ def cpu_model():
     return "unknown CPU"
 
 
-def cpu_baseline(c, sets0, seconds, threads=1):
+def cpu_baseline(c, sets0, seconds, workers=1):
     """The oracle, untuned, on the same first input set: whole rounds until
-    `seconds` of CPU time are spent (at least one), BLAS limited to
-    `threads`."""
+    `seconds` of wall time are spent (at least one).  BLAS runs on one
+    thread; with workers > 1 the oracle spreads its independent parts over
+    that many workers (the builder's draft positions on OpenMP threads, the
+    attention's (sequence, node) rows on worker processes), with the same
+    results."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
 
+    prev = oracle.set_threads(workers)
+    try:
+        return _cpu_rounds(c, sets0, seconds, np, threadpool_limits, oracle)
+    finally:
+        oracle.set_threads(prev)
+
+
+def _cpu_rounds(c, sets0, seconds, np, threadpool_limits, oracle):
+    """Whole oracle rounds on input set 0 until `seconds` have passed."""
     draft, target, q, k, v, roots, ctx = sets0
     b, N = target.shape[0], target.shape[1]
     mode = oracle.GREEDY if c["_T"] == 0 else oracle.SAMPLED
     rounds, t0 = 0, time.perf_counter()
-    with threadpool_limits(limits=threads):
+    with threadpool_limits(limits=1):
         while True:
             if c["build"]:
                 tr = oracle.tree_build(draft, c["k"], c["B"], roots, ctx)
@@ -219,6 +239,72 @@ def b_sweep(c, dev, stream, budgets=(16, 64, 128, 256, 512), L=4096, reps=50):
         torch.cuda.synchronize()
         out[B] = e0.elapsed_time(e1) / reps
     return out
+
+
+def attention_8b(dev, stream, rotate_gib=1.0, reps=100):
+    """The verification call at the 256-node shape (8B-class layer: 32 query /
+    8 KV heads, D=128, bf16, context 8192, the tree the builder makes from the
+    8B-class draft marginals: K=16, top-16, B=256), per call with HIP events
+    on its stream and the partial/combine split from the timing hook; Q/K/V
+    ~ N(0,1) drawn on the device from seeded generators, rotated over >= 1 GiB
+    of sets."""
+    import numpy as np
+    import torch
+
+    import tree_verification_best_amd as tv
+    import workloads
+
+    c = dict(workloads.CONFIGS["8b"])
+    b, N, L = 1, c["B"] + 1, c["L"]
+    draft, _ = workloads.logits(c, b, N)
+    roots = torch.from_numpy(workloads.root_tokens(c, b)).to(dev)
+    ctx = torch.full((b,), L, dtype=torch.int32, device=dev)
+    tree = tv.tv_tree_build(torch.from_numpy(draft).to(dev), c["k"], c["B"], roots, ctx)
+    cap = L + N
+    per_set = 2 * (2 * c["Hkv"] * cap * c["D"] + N * c["Hq"] * c["D"])
+    nsets = max(2, math.ceil(rotate_gib * 2 ** 30 / per_set))
+    sets = []
+    for i in range(nsets):
+        g = torch.Generator(device=dev)
+        g.manual_seed(880000 + i)
+        sets.append([torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+                     for shape in ((b, N, c["Hq"], c["D"]), (b, c["Hkv"], cap, c["D"]),
+                                   (b, c["Hkv"], cap, c["D"]))])
+    ws = torch.empty(tv.attention_workspace(b, N, c["Hq"], c["Hkv"], c["D"], L),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((b, N, c["Hq"], c["D"]), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((b, N, c["Hq"]), dtype=torch.float32, device=dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for e in evs:
+        e[1].record(stream)
+    for i in range(reps + 5):
+        q, k, v = sets[i % nsets]
+        if i >= 5:
+            evs[i - 5][0].record(stream)
+            tv.lib().tv_debug_set_attention_event(evs[i - 5][1].cuda_event)
+        tv.tv_tree_attention_verify(q, k, v, ctx, tree["anc"], tree["n_nodes"], L, workspace=ws,
+                                    out=out, lse=lse)
+        if i >= 5:
+            tv.lib().tv_debug_set_attention_event(None)
+            evs[i - 5][2].record(stream)
+    torch.cuda.synchronize()
+    call = sum(e[0].elapsed_time(e[2]) for e in evs) / reps
+    part = sum(e[0].elapsed_time(e[1]) for e in evs) / reps
+    comb = sum(e[1].elapsed_time(e[2]) for e in evs) / reps
+    flops = attention_flops(c, tree["n_nodes"].cpu().numpy(), tree["depth"].cpu().numpy(),
+                            ctx.cpu().numpy())
+    byts = algorithmic_bytes(c, b, N, L, False)["attention"]
+
+    def tf(ms):
+        return flops / (ms * 1e-3) / 1e12
+
+    return dict(ms=round(call, 5), algorithmic_MB=round(byts / 1e6, 3),
+                GBps=round(byts / (call * 1e-3) / 1e9, 1), GFLOP=round(flops / 1e9, 3),
+                TFLOPs=round(tf(call), 2), mfma_frac=round(tf(call) / MFMA_BF16_PEAK_TFLOPS, 4),
+                kernel_ms={"k_attn_partial": round(part, 5), "k_attn_combine": round(comb, 5)},
+                kernel_TFLOPs=round(tf(part), 2),
+                kernel_mfma_frac=round(tf(part) / MFMA_BF16_PEAK_TFLOPS, 4),
+                input_sets=nsets, nodes=int(tree["n_nodes"][0].item()))
 
 
 def main():
@@ -319,9 +405,13 @@ def main():
                                  out=dict(depth=tree["depth"], pos=tree["pos"], anc=tree["anc"]))
         if ev is not None:
             ev[1].record(stream)
+        if ev is not None and bf:
+            tv.lib().tv_debug_set_attention_event(ev[4].cuda_event)
         tv.tv_tree_attention_verify(s["q"], s["k"], s["v"], s["ctx"], tree["anc"], tree["n_nodes"],
                                     max_ctx, workspace=ws_a, out=attn_out, lse=lse)
         if ev is not None:
+            if bf:
+                tv.lib().tv_debug_set_attention_event(None)
             ev[2].record(stream)
         tv.tv_tree_accept(s["target"], tree["parent"], tree["token"], tree["depth"], tree["n_nodes"],
                           mode=mode, temperature=max(args.temperature, 1e-3), seed=1234, round=step,
@@ -336,9 +426,15 @@ def main():
         tv.tv_kv_commit(s["k"], s["v"], s["ctx"], acc["accept_len"], acc["accepted_nodes"],
                         new_ctx_len=new_ctx)
 
+    # every timed eager step adds its accept lengths on the device (after the
+    # step's last event, so outside the per-call brackets)
+    acc_sum = torch.zeros((b,), dtype=torch.int64, device=dev)
+
     def eager_steps(first, n, evs=None):
         for i in range(n):
             round_(first + i, evs[i] if evs is not None else None)
+            if evs is not None:
+                acc_sum.add_(acc["accept_len"])
 
     for i in range(args.warmup):
         round_(i)
@@ -347,6 +443,7 @@ def main():
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     graph_ms = None
+    batch_ms = []
     wall = 0.0
     if not args.eager:
         # the timed region: replays of the round captured once per input set
@@ -360,19 +457,34 @@ def main():
         for i in range(min(args.warmup, 2 * nsets)):
             graphs[i % nsets].replay()
         torch.cuda.synchronize()
+        # five equal batches of the K steps, each bracketed by events (the
+        # events add no work): their median is reported beside the mean
+        nb = 5 if args.steps >= 5 else 1
+        edges = [round(j * args.steps / nb) for j in range(nb + 1)]
+        bev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
         t0 = time.perf_counter()
         start.record(stream)
-        for i in range(args.steps):
-            graphs[i % nsets].replay()
+        for j in range(nb):
+            bev[j].record(stream)
+            for i in range(edges[j], edges[j + 1]):
+                graphs[i % nsets].replay()
+        bev[nb].record(stream)
         end.record(stream)
         torch.cuda.synchronize()
         wall += time.perf_counter() - t0
         graph_ms = start.elapsed_time(end) / args.steps
+        batch_ms = [bev[j].elapsed_time(bev[j + 1]) / (edges[j + 1] - edges[j]) for j in range(nb)]
 
     # eager launches of the same steps with HIP events around every call on
     # the stream the calls run on (events cannot be recorded inside a graph
     # on this platform): the per-call times and the roofline come from here
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # evs[i]: before build, after build, after attention, after accept, and
+    # (bf16) between the attention's partial and combine kernels, recorded by
+    # the library through its timing hook; each event is recorded once here
+    # so that it exists before its handle is passed on
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for e in evs:
+        e[4].record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
@@ -386,7 +498,17 @@ def main():
     calls = {}
     for name, (a, z) in (("build", (0, 1)), ("attention", (1, 2)), ("accept", (2, 3))):
         calls[name] = sum(evs[i][a].elapsed_time(evs[i][z]) for i in range(args.steps)) / args.steps
+    kern = {}
+    if bf:
+        # event to event on the call's stream: the partial kernel (from the
+        # event before the call) and the combine (to the event after it)
+        kern["k_attn_partial"] = sum(evs[i][1].elapsed_time(evs[i][4])
+                                     for i in range(args.steps)) / args.steps
+        kern["k_attn_combine"] = sum(evs[i][4].elapsed_time(evs[i][2])
+                                     for i in range(args.steps)) / args.steps
+    mean_accept = float(acc_sum.sum().item()) / (args.steps * b)
     sweep = {}
+    att8 = None
     if not args.round_only:
         # verification with the rotary embedding fused (queries and tree keys
         # turned at the tree's position ids), per call with events like the plain
@@ -427,6 +549,8 @@ def main():
         # figure): one sequence with this workload's heads, context 4096, random
         # trees of B + 1 nodes, per call with events
         sweep = b_sweep(c, dev, stream)
+        if args.workload != "8b" and bf:
+            att8 = attention_8b(dev, stream, args.rotate_gib)
         if c["build"]:
             # the cost-aware tree size over the last step's tree; the cost of n
             # draft nodes is the measured verification time, interpolated
@@ -516,41 +640,67 @@ def main():
             tf = aflops / (calls[name] * 1e-3) / 1e12
             per_call[name]["TFLOPs"] = round(tf, 2)
             per_call[name]["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+    if att8 is not None:
+        per_call["attention_8b"] = att8
     if "attention" in calls:
-        # the verification pass: HBM-bound below the ridge point, else MFMA
+        # the verification pass: HBM-bound below the ridge point, else MFMA.
+        # The dominant kernel is k_attn_partial: it reads every input of the
+        # call once (K/V rows, Q, the ancestor rows); the combine writes O and
+        # the lse.  achieved = its algorithmic bytes (or the call's flops) over
+        # its own event-to-event time; the whole call's figure is beside it.
         ms = calls["attention"]
         ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
         intensity = aflops / abytes["attention"]
+        out_bytes = b * N * c["Hq"] * (c["D"] * el + 4)
+        kbytes = abytes["attention"] - out_bytes
+        kms = kern.get("k_attn_partial", ms)
         traffic = recorded_traffic(args.workload)
-        if intensity < ridge:
-            gbs = abytes["attention"] / (ms * 1e-3) / 1e9
-            roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
-        else:
-            tf = aflops / (ms * 1e-3) / 1e12
-            roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
-        roof.update({"traffic": traffic, "call": "tv_tree_attention_verify",
-                     "kernels": "k_attn_partial+k_attn_combine", "ms": round(ms, 5),
-                     "algorithmic_bytes": abytes["attention"], "algorithmic_flops": aflops,
-                     "intensity_flop_per_byte": round(intensity, 1)})
+        hbm = intensity < ridge
+
+        def fig(nbytes, t):
+            if hbm:
+                a = nbytes / (t * 1e-3) / 1e9
+                return round(a, 1), round(a / HBM_PEAK_GBS, 4)
+            a = aflops / (t * 1e-3) / 1e12
+            return round(a, 2), round(a / MFMA_BF16_PEAK_TFLOPS, 4)
+
+        ach, frac = fig(kbytes, kms)
+        cach, cfrac = fig(abytes["attention"], ms)
+        roof = {"bound": "hbm" if hbm else "mfma", "achieved": ach,
+                "peak": HBM_PEAK_GBS if hbm else MFMA_BF16_PEAK_TFLOPS,
+                "unit": "GB/s" if hbm else "TFLOP/s", "frac": frac, "traffic": traffic,
+                "kernel": "k_attn_partial" if bf else "k_attn_f32", "kernel_ms": round(kms, 5),
+                "kernel_algorithmic_bytes": kbytes,
+                "call": {"name": "tv_tree_attention_verify", "ms": round(ms, 5),
+                         "achieved": cach, "frac": cfrac,
+                         "algorithmic_bytes": abytes["attention"],
+                         "kernels_ms": {k: round(v, 5) for k, v in kern.items()}},
+                "algorithmic_flops": aflops,
+                "intensity_flop_per_byte": round(intensity, 1)}
+        if bf:
+            # both kernels, without the gaps between and around them
+            pair = kern["k_attn_partial"] + kern["k_attn_combine"]
+            roof["call"]["kernels_frac"] = fig(abytes["attention"], pair)[1]
 
     cpu = cpu_all = None
     if not args.no_cpu_baseline:
         model = cpu_model()
-        r, dt = cpu_baseline(c, first, args.cpu_seconds, threads=1)
+        r, dt = cpu_baseline(c, first, args.cpu_seconds, workers=1)
         cpu = {"value": round(r / dt * rows, 1), "unit": "node-heads/s", "cores": 1,
                "kind": "oracle",
                "sample": f"{r} whole round(s) of the {args.workload} workload (input set 0), "
                          f"{dt:.1f} s, single thread (BLAS limited to 1), {model}"}
-        # the same with the BLAS pool on every host core this process may use
-        # (at most 16, the host share of one GPU); the oracle's C parts stay
-        # single-threaded
-        ncores = min(16, len(os.sched_getaffinity(0)))
-        r, dt = cpu_baseline(c, first, args.cpu_seconds, threads=ncores)
+        # the same spread over the host cores this process may use, at most
+        # 16 (one GPU's share of the host); `affinity_cores` is the uncapped
+        # count
+        affinity = len(os.sched_getaffinity(0))
+        ncores = min(16, affinity)
+        r, dt = cpu_baseline(c, first, args.cpu_seconds, workers=ncores)
         cpu_all = {"value": round(r / dt * rows, 1), "unit": "node-heads/s", "cores": ncores,
-                   "kind": "oracle",
-                   "sample": f"{r} whole round(s), {dt:.1f} s, BLAS on {ncores} threads"}
+                   "affinity_cores": affinity, "kind": "oracle",
+                   "sample": f"{r} whole round(s), {dt:.1f} s, {ncores} workers (draft "
+                             f"positions on OpenMP threads, attention rows on processes), "
+                             f"BLAS 1 thread each"}
 
     res = {
         "metric": "verify rounds/s as tree node x query-head rows verified per second",
@@ -571,10 +721,13 @@ def main():
                    "rounds_per_s": round(rounds_per_s, 2), "nodes": N,
                    "input_sets": nsets, "graph": not args.eager,
                    "eager_ms_per_step": round(eager_ms, 5),
+                   "batch_ms": [round(x, 5) for x in batch_ms],
+                   "batch_ms_median": round(sorted(batch_ms)[len(batch_ms) // 2], 5) if batch_ms else None,
                    "round_algorithmic_MB": round(sum(abytes[n] for n in ("build", "attention", "accept")
                                                      if n in abytes) / 1e6, 2),
                    "attention_GFLOP": round(aflops / 1e9, 3),
-                   "mean_accept_len": float(acc["accept_len"].float().mean().item()),
+                   "mean_accept_len": round(mean_accept, 4),
+                   "accept_len_samples": args.steps * b,
                    "per_call": per_call, "wall_s": round(wall, 3),
                    "b_sweep_ms": {str(k): round(v, 5) for k, v in sweep.items()},
                    "cpu_all_cores": cpu_all},

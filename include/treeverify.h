@@ -30,8 +30,9 @@
  *     (except overlapping tv_tree_build_noalloc calls on one GPU, which
  *     share that GPU's scratch buffer; for
  *     large budgets tv_tree_build raises its selection kernel's dynamic-LDS
- *     limit in the HIP runtime, an idempotent setting; the test hook
- *     tv_debug_set_spin_limit changes a process-wide setting).
+ *     limit in the HIP runtime, an idempotent setting; the test hooks
+ *     tv_debug_set_spin_limit and tv_debug_set_attention_event change
+ *     process-wide settings).
  *   - Arguments are checked on the host before any launch; a bad argument
  *     returns TV_ERR_INVALID (or TV_ERR_UNSUPPORTED for a valid request this
  *     build does not serve) and launches nothing.  A launch failure
@@ -72,12 +73,25 @@ typedef enum {
     TV_ERR_INVALID = 1,     /* bad pointer, size or combination of arguments */
     TV_ERR_UNSUPPORTED = 2, /* valid, but outside what this build serves      */
     TV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required     */
-    TV_ERR_DEVICE = 4       /* the HIP runtime reported a launch error        */
+    TV_ERR_DEVICE = 4,      /* the HIP runtime reported a launch error        */
+    TV_STATUS_RANGE_LO_ = INT32_MIN, TV_STATUS_RANGE_HI_ = INT32_MAX
 } tv_status;
 
-typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
-typedef enum { TV_GREEDY = 0, TV_SAMPLED = 1 } tv_accept_mode;
-typedef enum { TV_PROPOSAL_POINT_MASS = 0, TV_PROPOSAL_DRAFT = 1 } tv_proposal;
+/* The *_RANGE_* members are not values of the interface: they give every
+ * enum the range of int32, so that any int32 a caller passes (and the
+ * library rejects) is a valid value of the type in C and in C++. */
+typedef enum {
+    TV_F32 = 0, TV_BF16 = 1,
+    TV_DTYPE_RANGE_LO_ = INT32_MIN, TV_DTYPE_RANGE_HI_ = INT32_MAX
+} tv_dtype;
+typedef enum {
+    TV_GREEDY = 0, TV_SAMPLED = 1,
+    TV_MODE_RANGE_LO_ = INT32_MIN, TV_MODE_RANGE_HI_ = INT32_MAX
+} tv_accept_mode;
+typedef enum {
+    TV_PROPOSAL_POINT_MASS = 0, TV_PROPOSAL_DRAFT = 1,
+    TV_PROPOSAL_RANGE_LO_ = INT32_MIN, TV_PROPOSAL_RANGE_HI_ = INT32_MAX
+} tv_proposal;
 
 /* Limits of this build. */
 #define TV_MAX_VOCAB (1 << 18)
@@ -99,6 +113,14 @@ int tv_version(void);
  * are capped there).  0 sends nearly every block down that path, which
  * gives the same results.  Process-wide; returns the previous value. */
 int tv_debug_set_spin_limit(int polls);
+
+/* Test hook for timing: when `ev` is not null, every later bf16
+ * tv_tree_attention_verify(_rope) call records `ev` on its stream between
+ * its two kernels (the split partials and their combine), so that events
+ * recorded by the caller before and after the call bracket each kernel.
+ * null (the default) records nothing.  Process-wide; the caller keeps `ev`
+ * valid while it is set.  Returns TV_OK. */
+tv_status tv_debug_set_attention_event(hipEvent_t ev);
 
 /* ------------------------------------------------------------------------
  * tv_tree_build -- draft tree from per-position draft marginals.

@@ -71,8 +71,31 @@ def lib():
                                   _i32p, _i32p, _i32p, _i32p, c.c_int, c.c_float, c.c_int,
                                   c.c_uint64, c.c_uint64, c.c_int, _i32p, _i32p, _i32p]
     L.tvo_tree_accept.restype = c.c_int
+    L.tvo_set_threads.argtypes = [c.c_int]
+    L.tvo_set_threads.restype = c.c_int
+    L.tvo_set_threads(_threads)
     _lib = L
     return L
+
+
+_threads = 1
+
+
+def set_threads(n):
+    """Threads for the independent parts of a round: the draft positions of
+    the builder (OpenMP in oracle.c) and the (sequence, node) rows of the
+    attention (a thread pool).  Each part is computed exactly as with one
+    thread, so results do not depend on this.  Returns the previous value."""
+    global _threads
+    prev = _threads
+    _threads = max(1, int(n))
+    if _lib is not None:
+        _lib.tvo_set_threads(_threads)
+    return prev
+
+
+def threads():
+    return _threads
 
 
 def _f32(a):

@@ -10,16 +10,18 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "_liboracle.so")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, lib: str = LIB, cc: str = "gcc", flags=()) -> str:
+    """Compile oracle.c into `lib` (another compiler and extra flags serve a
+    sanitizer build into another path)."""
     src = os.path.join(HERE, "oracle.c")
-    tmp = LIB + ".tmp"
-    cmd = ["gcc", "-O2", "-std=gnu11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
-           "-shared", "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
+    tmp = lib + ".tmp"
+    cmd = [cc, "-O2", "-std=gnu11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+           "-shared", "-Wall", "-Wextra", "-fopenmp"] + list(flags) + ["-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -235,35 +235,60 @@ int tvo_topk(const float *row, int V, int k, int32_t *ids, float *vals)
 /* For each of the K positions: top-k tokens by logit, their drafter
  * probability q = W / Z at the build temperature, then re-sorted by
  * (q desc, id asc) -- rank r of a position is its index in this order. */
+static int position_candidates(const float *row, int V, int k, float inv_t, int32_t *cand_tok,
+                               double *cand_q, uint64_t *Z_out)
+{
+    int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)k);
+    if (!ids || !c) { free(ids); free(c); return TVO_ERR; }
+    tvo_topk(row, V, k, ids, NULL);
+    float m = row_max(row, V);
+    uint64_t Z = tvo_row_weights(row, V, inv_t, NULL);
+    for (int i = 0; i < k; ++i) {
+        uint64_t w = tvo_weight(row[ids[i]], m, inv_t);
+        c[i].id = ids[i];
+        c[i].val = row[ids[i]];
+        c[i].q = (double)w / (double)Z;
+    }
+    qsort(c, (size_t)k, sizeof(cand_t), cmp_q_desc_id_asc);
+    for (int i = 0; i < k; ++i) {
+        cand_tok[i] = c[i].id;
+        cand_q[i] = c[i].q;
+    }
+    if (Z_out) *Z_out = Z;
+    free(ids);
+    free(c);
+    return TVO_OK;
+}
+
+/* Threads for the positions of tvo_draft_candidates (1 = none).  The
+ * positions are independent and each is computed exactly as alone, so the
+ * results do not depend on this setting. */
+static int g_threads = 1;
+
+int tvo_set_threads(int n)
+{
+    int prev = g_threads;
+    g_threads = n < 1 ? 1 : n;
+    return prev;
+}
+
 int tvo_draft_candidates(const float *draft, int K, int V, int k, float build_temp,
                          int32_t *cand_tok, double *cand_q, uint64_t *Z_out)
 {
     if (K < 1 || V < 1 || k < 1 || k > V || !(build_temp > 0.0f)) return TVO_ERR;
     float inv_t = 1.0f / build_temp;
-    int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
-    cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)k);
-    if (!ids || !c) { free(ids); free(c); return TVO_ERR; }
+    int rc = TVO_OK;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(g_threads) if (g_threads > 1)
     for (int j = 0; j < K; ++j) {
-        const float *row = draft + (size_t)j * (size_t)V;
-        tvo_topk(row, V, k, ids, NULL);
-        float m = row_max(row, V);
-        uint64_t Z = tvo_row_weights(row, V, inv_t, NULL);
-        for (int i = 0; i < k; ++i) {
-            uint64_t w = tvo_weight(row[ids[i]], m, inv_t);
-            c[i].id = ids[i];
-            c[i].val = row[ids[i]];
-            c[i].q = (double)w / (double)Z;
+        if (position_candidates(draft + (size_t)j * (size_t)V, V, k, inv_t,
+                                cand_tok + (size_t)j * k, cand_q + (size_t)j * k,
+                                Z_out ? Z_out + j : NULL)) {
+#pragma omp atomic write
+            rc = TVO_ERR;
         }
-        qsort(c, (size_t)k, sizeof(cand_t), cmp_q_desc_id_asc);
-        for (int i = 0; i < k; ++i) {
-            cand_tok[(size_t)j * k + i] = c[i].id;
-            cand_q[(size_t)j * k + i] = c[i].q;
-        }
-        if (Z_out) Z_out[j] = Z;
     }
-    free(ids);
-    free(c);
-    return TVO_OK;
+    return rc;
 }
 
 /* ------------------------------------------------------------------------- */

@@ -33,9 +33,10 @@ SOURCES = {
 }
 
 
-def _compile(src, extra, verbose):
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = ["hipcc"] + COMMON + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, extra, verbose, objdir=BUILD, host_flags=()):
+    obj = os.path.join(objdir, src + ".o")
+    host = [f for flag in host_flags for f in ("-Xarch_host", flag)]
+    cmd = ["hipcc"] + COMMON + extra + host + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -48,17 +49,22 @@ def _compile(src, extra, verbose):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, lib: str = LIB, objdir: str = BUILD, host_flags=()) -> str:
+    """Compile every source and link `lib`.  `host_flags` go to the host
+    compilation and the link only (e.g. a sanitizer build of the host code
+    into another directory); the device code is the same."""
+    os.makedirs(objdir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
-        objs = list(ex.map(lambda kv: _compile(kv[0], kv[1], verbose), SOURCES.items()))
-    tmp = LIB + ".tmp"
-    cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+        objs = list(ex.map(lambda kv: _compile(kv[0], kv[1], verbose, objdir, host_flags),
+                           SOURCES.items()))
+    tmp = lib + ".tmp"
+    cmd = (["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC"] + list(host_flags) +
+           ["-o", tmp] + objs)
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

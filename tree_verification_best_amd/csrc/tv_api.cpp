@@ -100,6 +100,7 @@ const char* tv_status_string(tv_status s) {
     case TV_ERR_UNSUPPORTED: return "TV_ERR_UNSUPPORTED: outside the limits of this build";
     case TV_ERR_WORKSPACE: return "TV_ERR_WORKSPACE: workspace missing or too small";
     case TV_ERR_DEVICE: return "TV_ERR_DEVICE: HIP launch error";
+    default: break;
   }
   return "unknown tv_status";
 }
@@ -348,6 +349,11 @@ tv_status tv_kv_commit(void* k_cache, void* v_cache, tv_dtype dt, int batch, int
 }
 
 int tv_debug_set_spin_limit(int polls) { return tvk::set_rowstat_spin_limit(polls); }
+
+tv_status tv_debug_set_attention_event(hipEvent_t ev) {
+  tvk::set_attention_mid_event(ev);
+  return TV_OK;
+}
 
 tv_status tv_kv_commit_rope(void* k_cache, void* v_cache, tv_dtype dt, int batch, int Hkv,
                             int cap, int D, const int32_t* ctx_len, const int32_t* accept_len,

@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "tv_device.h"
 #include "tv_internal.h"
 
@@ -773,6 +775,12 @@ AttnPlan attention_plan(int batch, int N, int Hq, int Hkv, int D, int max_ctx, i
   return p;
 }
 
+namespace {
+std::atomic<hipEvent_t> g_mid_event{nullptr};
+}  // namespace
+
+hipEvent_t set_attention_mid_event(hipEvent_t ev) { return g_mid_event.exchange(ev); }
+
 hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, const void* v,
                             bool bf16, const int* ctx_len, const uint64_t* anc,
                             const int* n_nodes, int batch, int N, int Hq, int Hkv, int D,
@@ -823,6 +831,10 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, con
       TV_PARTIAL(64, false);
   }
 #undef TV_PARTIAL
+  if (hipEvent_t ev = g_mid_event.load(std::memory_order_relaxed)) {
+    const hipError_t e = hipEventRecord(ev, stream);
+    if (e != hipSuccess) return e;
+  }
   const unsigned cgrid = (unsigned)((rows + (256 / (D / 8)) - 1) / (256 / (D / 8)));
   if (out_f32)
     hipLaunchKernelGGL((k_attn_combine<float>), dim3(cgrid), dim3(256), 0, stream, Opart, Mpart,

@@ -62,6 +62,9 @@ struct AttnPlan {
 };
 
 AttnPlan attention_plan(int batch, int N, int Hq, int Hkv, int D, int max_ctx, int splits);
+// Timing hook: an event recorded between the partial and combine kernels
+// (nullptr: none).  Returns the previous one.
+hipEvent_t set_attention_mid_event(hipEvent_t ev);
 hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, const void* v,
                             bool bf16, const int* ctx_len, const uint64_t* anc,
                             const int* n_nodes, int batch, int N, int Hq, int Hkv, int D,
