@@ -122,6 +122,18 @@ int tv_debug_set_spin_limit(int polls);
  * valid while it is set.  Returns TV_OK. */
 tv_status tv_debug_set_attention_event(hipEvent_t ev);
 
+/* Test hook: the fixed-point softmax weight that the builder and the
+ * acceptance kernels give a logit (the primer's "acceptance and rejection":
+ * the target and draft distributions as softmax weights; TAPS sec. 4.2: the
+ * drafter's probabilities), for the `count` fp32 values whose bit patterns
+ * are first_bits, first_bits + 1, ..., as logits of a row with maximum
+ * row_max at inverse temperature inv_t.  unit != 0 selects the form the row
+ * passes use when inv_t == 1 (then inv_t must be 1).  out: uint64 [count],
+ * device.  TV_ERR_INVALID for a null out, count 0, a non-finite row_max or
+ * inv_t <= 0. */
+tv_status tv_debug_weights(uint32_t first_bits, uint32_t count, float row_max, float inv_t,
+                           int unit, uint64_t *out, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * tv_tree_build -- draft tree from per-position draft marginals.
  *

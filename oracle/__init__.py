@@ -71,6 +71,8 @@ def lib():
                                   _i32p, _i32p, _i32p, _i32p, c.c_int, c.c_float, c.c_int,
                                   c.c_uint64, c.c_uint64, c.c_int, _i32p, _i32p, _i32p]
     L.tvo_tree_accept.restype = c.c_int
+    L.tvo_weight_range.argtypes = [c.c_uint32, c.c_int64, c.c_float, c.c_float, _u64p]
+    L.tvo_weight_range.restype = None
     L.tvo_set_threads.argtypes = [c.c_int]
     L.tvo_set_threads.restype = c.c_int
     L.tvo_set_threads(_threads)
@@ -125,6 +127,13 @@ def constants():
 def weight(logit, row_max, inv_t=1.0):
     return int(lib().tvo_weight(float(np.float32(logit)), float(np.float32(row_max)),
                                 float(np.float32(inv_t))))
+
+
+def weight_range(first_bits, count, row_max=0.0, inv_t=1.0):
+    """weight() of the `count` fp32 values with bit patterns first_bits, first_bits + 1, ..."""
+    out = np.empty(int(count), np.uint64)
+    lib().tvo_weight_range(int(first_bits), int(count), float(row_max), float(inv_t), out)
+    return out
 
 
 def row_weights(row, temperature=1.0):

@@ -115,6 +115,33 @@ uint64_t tvo_weight(float logit, float row_max, float inv_t)
     return (uint64_t)rintf(scaled);
 }
 
+/* Threads for the independent parts below -- the draft positions of
+ * tvo_draft_candidates and the values of tvo_weight_range (1 = none).  Each
+ * part is computed exactly as alone, so results do not depend on this. */
+static int g_threads = 1;
+
+int tvo_set_threads(int n)
+{
+    int prev = g_threads;
+    g_threads = n < 1 ? 1 : n;
+    return prev;
+}
+
+/* tvo_weight of every fp32 value whose bit pattern is first_bits + i,
+ * 0 <= i < count, as the logit (a helper for exhaustive comparisons). */
+
+void tvo_weight_range(uint32_t first_bits, int64_t count, float row_max_, float inv_t,
+                      uint64_t *out)
+{
+#pragma omp parallel for schedule(static) num_threads(g_threads) if (g_threads > 1)
+    for (int64_t i = 0; i < count; ++i) {
+        uint32_t bits = first_bits + (uint32_t)i;
+        float x;
+        memcpy(&x, &bits, sizeof x);
+        out[i] = tvo_weight(x, row_max_, inv_t);
+    }
+}
+
 static float row_max(const float *row, int V)
 {
     float m = row[0];
@@ -259,18 +286,6 @@ static int position_candidates(const float *row, int V, int k, float inv_t, int3
     free(ids);
     free(c);
     return TVO_OK;
-}
-
-/* Threads for the positions of tvo_draft_candidates (1 = none).  The
- * positions are independent and each is computed exactly as alone, so the
- * results do not depend on this setting. */
-static int g_threads = 1;
-
-int tvo_set_threads(int n)
-{
-    int prev = g_threads;
-    g_threads = n < 1 ? 1 : n;
-    return prev;
 }
 
 int tvo_draft_candidates(const float *draft, int K, int V, int k, float build_temp,

@@ -20,7 +20,7 @@ def _declared():
 
 def test_header_functions_exported():
     names = _declared()
-    assert len(names) == 20
+    assert len(names) == 21
     lib = ctypes.CDLL(tv.LIBPATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -319,3 +319,13 @@ def test_spin_limit_hook():
     assert L.tv_debug_set_spin_limit(10 ** 9) == 0
     assert L.tv_debug_set_spin_limit(-1) == 4096  # capped at the default
     assert L.tv_debug_set_spin_limit(-1) == 4096
+
+
+def test_debug_hooks_reject_on_host():
+    L = tv.lib()
+    assert L.tv_debug_weights(0, 16, 0.0, 1.0, 0, None, None) == tv.TV_ERR_INVALID
+    assert L.tv_debug_weights(0, 0, 0.0, 1.0, 0, FAKE, None) == tv.TV_ERR_INVALID
+    assert L.tv_debug_weights(0, 16, float("inf"), 1.0, 0, FAKE, None) == tv.TV_ERR_INVALID
+    assert L.tv_debug_weights(0, 16, 0.0, 0.0, 0, FAKE, None) == tv.TV_ERR_INVALID
+    assert L.tv_debug_weights(0, 16, 0.0, 0.7, 1, FAKE, None) == tv.TV_ERR_INVALID
+    assert L.tv_debug_set_attention_event(None) == tv.TV_OK

@@ -63,6 +63,11 @@ CASES = [
     ("many-splits", 1, 65, 8, 2, 128, [700], [65], "random", "bf16", 7),
     ("4b-heads", 1, 65, 32, 8, 128, [4096], [65], "random", "bf16", 0),
     ("wide-tree", 1, 257, 8, 2, 128, [300], [257], "random", "bf16", 0),
+    # more than 16 partials per row: the combine's batched path (22 and 33
+    # partials at explicit splits, 30 from the automatic choice at 32K)
+    ("partials-22", 1, 33, 8, 2, 128, [8000], [33], "random", "bf16", 24),
+    ("partials-33", 1, 33, 8, 2, 128, [8000], [30], "random", "bf16", 40),
+    ("partials-auto-32k", 1, 17, 32, 8, 128, [32768], [17], "random", "bf16", 0),
 ]
 
 
@@ -91,10 +96,7 @@ def test_attention_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("cfg", ["8b", "long"])
-def test_attention_full_size_sampled_rows(cfg):
-    """Full-size shapes in the automatic split configuration; the oracle checks
-    a sample of (node, all heads) rows one by one."""
+def _full_size(cfg):
     c = workloads.CONFIGS[cfg]
     N, L = c["B"] + 1, c["L"]
     cap = L + N
@@ -108,15 +110,39 @@ def test_attention_full_size_sampled_rows(cfg):
     out, lse = tv.tv_tree_attention_verify(bf16_dev(q), bf16_dev(k), bf16_dev(v), dev(ctx),
                                            dev(anc.view(np.int64)), dev(nn), L)
     torch.cuda.synchronize()
+    return (q, k, v, ctx, anc, nn), out, lse
+
+
+def test_attention_8b_full_tensor():
+    """The 256-node shape (context 8192, 32 query / 8 KV heads) in the
+    automatic split configuration: every one of the 257 x 32 rows against
+    the oracle (its rows spread over the host cores)."""
+    import os
+    inputs, out, lse = _full_size("8b")
+    prev = oracle.set_threads(min(16, len(os.sched_getaffinity(0))))
+    try:
+        ro, rl = oracle.tree_attention(*inputs)
+    finally:
+        oracle.set_threads(prev)
+    assert_attention_close(out, lse, ro, rl, inputs[5], "8b")
+
+
+def test_attention_long_sampled_rows():
+    """The 32K-context, 513-node shape: a sample of (node, all heads) rows
+    checked one by one."""
+    inputs, out, lse = _full_size("long")
+    q, k, v, ctx, anc, nn = inputs
+    N = int(nn[0])
     g = out.float().cpu().numpy()
     gl = lse.cpu().numpy()
-    rows = [(0, i) for i in (0, 1, N // 3, N // 2, N - 2, N - 1)]
-    ref = oracle.tree_attention_rows(q, k, v, ctx, anc, nn, rows)
+    r = np.random.default_rng(5)
+    picks = sorted(set([0, 1, N // 3, N // 2, N - 2, N - 1] + r.integers(2, N - 2, 18).tolist()))
+    ref = oracle.tree_attention_rows(q, k, v, ctx, anc, nn, [(0, i) for i in picks])
     for (s, i), (ro, rl) in ref.items():
         d = g[s, i] - ro
-        assert np.abs(d).max() <= 1e-2
-        assert np.linalg.norm(d) / np.linalg.norm(ro) <= 2e-2
-        assert np.abs(gl[s, i] - rl).max() <= 1e-2
+        assert np.abs(d).max() <= 1e-2, i
+        assert np.linalg.norm(d) / np.linalg.norm(ro) <= 2e-2, i
+        assert np.abs(gl[s, i] - rl).max() <= 1e-2, i
 
 
 def test_attention_bf16_output_is_rounded_fp32():

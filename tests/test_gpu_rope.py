@@ -100,8 +100,12 @@ def test_attention_rope_full_size_rows():
     rows = [(0, i) for i in (0, 1, 2, 77, 128, 200, N - 1)]
     ref = oracle.tree_attention_rope_rows(q, k, v, ctx, anc[None], nn, pos, 1e6, rows)
     g = host(out)
-    for (s, i), (o, _) in ref.items():
-        assert np.abs(g[s, i] - o).max() <= 1e-2, i
+    gl = host(lse)
+    for (s, i), (o, l) in ref.items():
+        d = g[s, i] - o
+        assert np.abs(d).max() <= 1e-2, i
+        assert np.linalg.norm(d) / np.linalg.norm(o) <= 2e-2, i
+        assert np.abs(gl[s, i] - l).max() <= 1e-2, i
 
 
 def _commit_case(r, b, Hkv, D, Ls, paths, width, cap, dt):

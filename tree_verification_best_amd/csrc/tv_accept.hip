@@ -1205,4 +1205,24 @@ hipError_t launch_accept(const AcceptPlan& p, const void* target, const void* dr
   return hipGetLastError();
 }
 
+// Test hook: the fixed-point weight of every fp32 value whose bit pattern is
+// first + i, 0 <= i < count, as the logit of a row with maximum m (the
+// inv_t == 1 form used by the row passes when unit is set).
+__global__ __launch_bounds__(256) void k_debug_weights(uint32_t first, uint32_t count, float m,
+                                                       float inv_t, int unit,
+                                                       uint64_t* __restrict__ out) {
+  const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  const float x = __builtin_bit_cast(float, first + (uint32_t)i);
+  out[i] = unit ? (uint64_t)weight_f<true>(x, m, inv_t) : weight(x, m, inv_t);
+}
+
+hipError_t launch_debug_weights(uint32_t first, uint32_t count, float m, float inv_t, bool unit,
+                                uint64_t* out, hipStream_t stream) {
+  const unsigned grid = (unsigned)(((uint64_t)count + 255) / 256);
+  hipLaunchKernelGGL(k_debug_weights, dim3(grid), dim3(256), 0, stream, first, count, m, inv_t,
+                     unit ? 1 : 0, out);
+  return hipGetLastError();
+}
+
 }  // namespace tvk

@@ -350,6 +350,14 @@ tv_status tv_kv_commit(void* k_cache, void* v_cache, tv_dtype dt, int batch, int
 
 int tv_debug_set_spin_limit(int polls) { return tvk::set_rowstat_spin_limit(polls); }
 
+tv_status tv_debug_weights(uint32_t first_bits, uint32_t count, float row_max, float inv_t,
+                           int unit, uint64_t* out, hipStream_t stream) {
+  if (!out || count < 1 || !std::isfinite(row_max) || !finite_pos(inv_t)) return TV_ERR_INVALID;
+  if (unit && inv_t != 1.0f) return TV_ERR_INVALID;
+  return device_status(
+      tvk::launch_debug_weights(first_bits, count, row_max, inv_t, unit != 0, out, stream));
+}
+
 tv_status tv_debug_set_attention_event(hipEvent_t ev) {
   tvk::set_attention_mid_event(ev);
   return TV_OK;

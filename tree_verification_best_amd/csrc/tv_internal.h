@@ -91,6 +91,8 @@ struct AcceptPlan {
 
 AcceptPlan accept_plan(int batch, int N, int K, int V, bool sampled, bool draft);
 int set_rowstat_spin_limit(int polls);  // < 0: the default; returns the previous limit
+hipError_t launch_debug_weights(uint32_t first, uint32_t count, float m, float inv_t, bool unit,
+                                uint64_t* out, hipStream_t stream);
 hipError_t launch_accept(const AcceptPlan& p, const void* target, const void* draft,
                          bool bf16, int batch, int N, int K, int V, const int* parent,
                          const int* token, const int* depth, const int* n_nodes, bool sampled,
