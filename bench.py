@@ -381,7 +381,7 @@ def main():
     mode = tv.TV_SAMPLED if sampled else tv.TV_GREEDY
     ws_b = torch.empty(max(tv.tree_build_workspace(b, K, V, c["k"], c["B"]), 1), dtype=torch.uint8, device=dev) if c["build"] else None
     ws_a = torch.empty(tv.attention_workspace(b, N, c["Hq"], c["Hkv"], c["D"], max_ctx), dtype=torch.uint8, device=dev)
-    ws_c = torch.empty(tv.accept_workspace(b, N, K, V, mode), dtype=torch.uint8, device=dev)
+    ws_c = torch.zeros(tv.accept_workspace(b, N, K, V, mode), dtype=torch.uint8, device=dev)
     attn_out = torch.empty((b, N, c["Hq"], c["D"]), dtype=tdt, device=dev)
     lse = torch.empty((b, N, c["Hq"]), dtype=torch.float32, device=dev)
     acc = dict(accept_len=torch.empty((b,), **i32), accepted_nodes=torch.empty((b, K + 1), **i32),

@@ -109,7 +109,7 @@ int tv_version(void);
 
 /* Test hook: the number of polls a block of tv_tree_accept's sampled row
  * pass makes while waiting for the other blocks of its row before it finds
- * the row maximum by itself (< 0 restores the default, 4096; larger values
+ * the row maximum by itself (< 0 restores the default, 48; larger values
  * are capped there).  0 sends nearly every block down that path, which
  * gives the same results.  Process-wide; returns the previous value. */
 int tv_debug_set_spin_limit(int polls);
@@ -359,9 +359,14 @@ tv_status tv_tree_attention_verify_rope(const void *q, const void *k_cache, cons
  * Sampled mode reads every logit row once: the blocks that hold the chunks
  * of one row wait for each other to agree on the row's maximum before they
  * weigh their chunks.  The grid is sized within what the device holds at
- * once, and the wait is bounded: a block that waits too long (other
- * work holding the device) re-reads its row to find the maximum itself, with
- * the same result, only slower.
+ * once, and the wait is bounded (tens of microseconds): a block that waits
+ * too long (other work holding the device) re-reads its row to find the
+ * maximum itself, with the same result, only slower.
+ * Workspace (sampled mode): zero-fill it once when it is allocated, and again
+ * before reusing it for another (batch, N, K, V, mode, proposal).  The row
+ * pass's hand-off words must be zero when a call starts; every call leaves
+ * them zero, so calls and replays of captured calls need no clearing.
+ * Greedy mode needs no particular contents.
  * ------------------------------------------------------------------------ */
 size_t tv_tree_accept_workspace(int batch, int N, int K, int V, tv_accept_mode mode,
                                 tv_proposal proposal);

@@ -315,10 +315,10 @@ def test_check_rejects():
 def test_spin_limit_hook():
     """The sampled row pass's wait bound: set, capped at the default, restored."""
     L = tv.lib()
-    assert L.tv_debug_set_spin_limit(0) == 4096
+    assert L.tv_debug_set_spin_limit(0) == 48
     assert L.tv_debug_set_spin_limit(10 ** 9) == 0
-    assert L.tv_debug_set_spin_limit(-1) == 4096  # capped at the default
-    assert L.tv_debug_set_spin_limit(-1) == 4096
+    assert L.tv_debug_set_spin_limit(-1) == 48  # capped at the default
+    assert L.tv_debug_set_spin_limit(-1) == 48
 
 
 def test_debug_hooks_reject_on_host():

@@ -228,6 +228,50 @@ def test_accept_replayable():
 
 
 @pytest.mark.parametrize("proposal", ["point_mass", "draft"])
+def test_accept_sampled_workspace_reuse(proposal):
+    """One zero-filled workspace serves consecutive sampled calls of one shape:
+    each call leaves the row pass's hand-off words zero for the next (no
+    clearing launch).  Every call matches the oracle."""
+    r = np.random.default_rng(31)
+    V = 151936
+    if proposal == "point_mass":
+        b, N, K = 2, 65, 16
+        prop = tv.TV_PROPOSAL_POINT_MASS
+    else:
+        b, K = 2, 5
+        N = K + 1
+        prop = tv.TV_PROPOSAL_DRAFT
+    ws = torch.zeros(tv.accept_workspace(b, N, K, V, tv.TV_SAMPLED, prop), dtype=torch.uint8,
+                     device="cuda")
+    for call in range(4):
+        if proposal == "point_mass":
+            parent, token, depth, n = _random_trees(r, b, N, V, 8, ns=[N, 30 + call])
+            target = workloads.plant((r.standard_normal((b, N, V)) * 3).astype(np.float32),
+                                     parent, token, n, 12.0)
+            draft, kw = None, dict(max_depth=int(depth.max()) + 1)
+        else:
+            base = (r.standard_normal((b, N, V)) * 2).astype(np.float32)
+            target = base + (0.3 * r.standard_normal((b, N, V))).astype(np.float32)
+            draft = base[:, :K] + r.standard_normal((b, K, V)).astype(np.float32)
+            parent = np.tile(np.arange(-1, N - 1, dtype=np.int32), (b, 1))
+            depth = np.tile(np.arange(N, dtype=np.int32), (b, 1))
+            token = r.integers(0, V, size=(b, N)).astype(np.int32)
+            for s_ in range(b):
+                for j in range(K):
+                    token[s_, j + 1] = int(np.argmax(draft[s_, j]))
+            n = np.full(b, N, np.int32)
+            kw = dict(max_depth=K, proposal=oracle.DRAFT)
+        g = tv.tv_tree_accept(dev(target), dev(parent), dev(token), dev(depth), dev(n),
+                              mode=tv.TV_SAMPLED, draft_logits=dev(draft) if draft is not None
+                              else None, temperature=1.0, seed=99, round=call, workspace=ws,
+                              **kw)
+        torch.cuda.synchronize()
+        o = oracle.tree_accept(target, parent, token, depth, n, mode=oracle.SAMPLED,
+                               draft=draft, temperature=1.0, seed=99, round=call, **kw)
+        assert_accept_equal(g, o, f"{proposal} call {call}")
+
+
+@pytest.mark.parametrize("proposal", ["point_mass", "draft"])
 def test_accept_row_pass_fallback(proposal):
     """The sampled row pass with its wait bound at 0 polls: nearly every block
     finds its row's maximum by reading the whole row itself.  The results are
@@ -278,11 +322,14 @@ def test_accept_concurrent_streams():
     kw = dict(mode=tv.TV_SAMPLED, seed=77, max_depth=int(depth.max()) + 1)
     streams = [torch.cuda.Stream() for _ in range(4)]
     torch.cuda.synchronize()
+    import time
+    t0 = time.perf_counter()
     outs = []
     for i, st in enumerate(streams):
         with torch.cuda.stream(st):
             outs.append(tv.tv_tree_accept(*args, round=i, **kw))
     torch.cuda.synchronize()
+    print(f"four concurrent sampled calls: {1e3 * (time.perf_counter() - t0):.2f} ms", flush=True)
     for i, g in enumerate(outs):
         o = oracle.tree_accept(target, parent, token, depth, n, mode=oracle.SAMPLED,
                                seed=77, round=i, max_depth=kw["max_depth"])

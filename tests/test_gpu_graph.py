@@ -48,7 +48,7 @@ def test_round_replays():
                       device="cuda")
     wsa = torch.empty(tv.attention_workspace(b, N, c["Hq"], c["Hkv"], c["D"], 1500),
                       dtype=torch.uint8, device="cuda")
-    wsc = torch.empty(tv.accept_workspace(b, N, K, V, tv.TV_SAMPLED), dtype=torch.uint8,
+    wsc = torch.zeros(tv.accept_workspace(b, N, K, V, tv.TV_SAMPLED), dtype=torch.uint8,
                       device="cuda")
     tree = tv.tv_tree_build(d, c["k"], c["B"], roots, ctx, workspace=wsb)
     out = torch.empty((b, N, c["Hq"], c["D"]), dtype=torch.bfloat16, device="cuda")

@@ -153,12 +153,15 @@ def _check(status, where):
         raise TreeVerifyError(status, where)
 
 
-def _workspace(nbytes, device, workspace):
+def _workspace(nbytes, device, workspace, zero=False):
+    """The caller's workspace, or a new one (zero-filled where the call needs
+    zeros in a new workspace)."""
     if workspace is not None:
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError("workspace too small")
         return workspace, workspace.numel() * workspace.element_size()
-    buf = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    make = torch.zeros if zero else torch.empty
+    buf = make(max(int(nbytes), 1), dtype=torch.uint8, device=device)
     return buf, buf.numel()
 
 
@@ -302,7 +305,7 @@ def tv_tree_accept(target_logits, parent, token, depth, n_nodes, *, mode, max_de
                    accepted_nodes=torch.empty((b, width), **i32),
                    out_tokens=torch.empty((b, width), **i32))
     need = L.tv_tree_accept_workspace(b, N, max(K, 1), V, mode, proposal)
-    ws, wsb = _workspace(need, dev, workspace)
+    ws, wsb = _workspace(need, dev, workspace, zero=mode == TV_SAMPLED)
     dptr = _dev(draft_logits, "draft_logits", target_logits.dtype) if draft_logits is not None else None
     st = L.tv_tree_accept(_dev(target_logits, "target_logits"), dptr, _dt(target_logits), b, N,
                           K, V, _dev(parent, "parent", torch.int32),

@@ -11,7 +11,6 @@
 //   k_rowmax       grid (chunks, rows)  greedy: (max, argmax) of each
 //                                       4096-token chunk of every target row,
 //                                       stored chunk-major
-//   k_zero_slots   grid (rows * Cb)     sampled: clears the row pass's slots
 //   k_rowstat      grid (J * Cb)        sampled: one pass over every target
 //                                       row (and draft row in DRAFT mode) that
 //                                       keeps its span of the row in registers
@@ -251,7 +250,10 @@ __device__ __forceinline__ void chunk_mass(const float (&x)[E], const T* p, int 
 // the same: a block that has polled spin_limit times in vain (other work
 // holding the device, say) takes the row maximum from the whole row itself,
 // which gives the same value, so the results never depend on the schedule.
-// The slots must be zero at the start (k_zero_slots runs first); each row's
+// The slots and the rows' mass accumulators must be zero at the start: a
+// new workspace is zero-filled by its owner, and k_walk, the call's last
+// reader of them, returns them to zero (so no clearing launch is needed and
+// replays of a captured call find them as the first call did).  Each row's
 // slots start on a 256-byte line of their own.
 template <int E>
 __device__ __forceinline__ void post_span_max(const float (&x)[E], float* sv, float* cmax,
@@ -375,15 +377,6 @@ __global__ __launch_bounds__(kAccNT) void k_rowstat(const T* __restrict__ target
       }
     }
   }
-}
-
-// zeroes the Cb slots of every row (rows of `stride` words) and the rows'
-// mass accumulators
-__global__ void k_zero_slots(uint64_t* __restrict__ slot, int64_t rows, int Cb, int stride,
-                             uint64_t* __restrict__ rowz) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < rows * Cb) slot[(i / Cb) * stride + i % Cb] = 0;
-  if (i < rows) rowz[i * kRowzStride] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -515,7 +508,7 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
     const int* __restrict__ depth, const int* __restrict__ n_nodes, float inv_t,
     uint64_t seed, uint64_t round, int max_depth, const float* __restrict__ cmax,
     const int* __restrict__ carg, const uint64_t* __restrict__ cz,
-    const float* __restrict__ rowm, const uint64_t* __restrict__ rowz,
+    const float* __restrict__ rowm, uint64_t* rowz, uint64_t* slot, int slot_stride, int Cb,
     const uint64_t* __restrict__ wtg, const uint64_t* __restrict__ wqg, int64_t trows,
     int64_t rows, int* __restrict__ accept_len, int* __restrict__ accepted_nodes,
     int* __restrict__ out_tokens, DraftPending* __restrict__ pend) {
@@ -573,13 +566,29 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
   constexpr int kRowsPer = (kMaxN + kMaxDraftRows + kAccNT - 1) / kAccNT;
   float tmv[kRowsPer];
   uint64_t tzv[kRowsPer];
+  // the root row's chunk masses, for a final draw at the root (the usual
+  // end of a walk): wave 0, lane j < C holds chunk j
+  uint64_t cz_root = 0;
   if constexpr (kSampled) {
+    if (wave == 0 && lane < C) cz_root = cz[(int64_t)lane * rows + rb];
 #pragma unroll
     for (int k = 0; k < kRowsPer; ++k) {
       const int r = tid + k * kAccNT;
       const int64_t grow = r >= nr ? 0 : (r < N ? rb + r : trows + (int64_t)b * K + (r - N));
       tmv[k] = rowm[grow];
       tzv[k] = rowz[grow * kRowzStride];
+    }
+    // the row pass's hand-off state of this sequence's rows goes back to
+    // zero for the next call (each thread clears what it has just read; the
+    // spans' slots are not read after the row pass)
+#pragma unroll
+    for (int k = 0; k < kRowsPer; ++k) {
+      const int r = tid + k * kAccNT;
+      if (r < nr) {
+        const int64_t grow = r < N ? rb + r : trows + (int64_t)b * K + (r - N);
+        rowz[grow * kRowzStride] = 0;
+        for (int c = 0; c < Cb; ++c) slot[grow * slot_stride + c] = 0;
+      }
     }
   } else {
     load_batch(0, part);
@@ -847,7 +856,7 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
     const int nk = (MODE == kPointMass && len < max_depth) ? sh.off[u + 1] - o0 : 0;
     if (wave == 0) {
       const int jl = lane < C ? lane : 0;
-      const uint64_t czu = cz[(int64_t)jl * rows + grow];
+      const uint64_t czu = u == 0 ? cz_root : cz[(int64_t)jl * rows + grow];
       uint64_t d0, d1;
       if (u < kAccNT) {
         d0 = sh.rd0[u];
@@ -1054,9 +1063,11 @@ AcceptPlan accept_plan(int batch, int N, int K, int V, bool sampled, bool draft)
 }
 
 // Polls of the row-maximum wait before a k_rowstat block reads the whole row
-// itself (about 1 us each).  tv_debug_set_spin_limit lowers it so that tests
-// take the fallback.
-constexpr int kSpinLimit = 1 << 12;
+// itself (each an agent-scope load, about 1 us under the pass's traffic):
+// tens of microseconds, against the few polls a resident group needs, so
+// that a block delayed by other work on the device costs a bounded detour.
+// tv_debug_set_spin_limit lowers it so that tests take the fallback.
+constexpr int kSpinLimit = 48;
 std::atomic<int> g_rowstat_spin_limit{kSpinLimit};
 
 int set_rowstat_spin_limit(int polls) {
@@ -1141,15 +1152,13 @@ static void launch_accept_t(const AcceptPlan& p, const T* target, const T* draft
       draft_proposal ? reinterpret_cast<DraftPending*>(w + p.off_pend) : nullptr;
   uint64_t* rowz = sampled ? reinterpret_cast<uint64_t*>(w + p.off_rowz) : nullptr;
   float* rowm = sampled ? reinterpret_cast<float*>(w + p.off_rowm) : nullptr;
+  uint64_t* slot = sampled ? reinterpret_cast<uint64_t*>(w + p.off_slot) : nullptr;
   const int64_t trows = (int64_t)batch * N;
   const dim3 g(p.C, (unsigned)p.rows);
   const dim3 blk(kAccNT);
+  RowstatShape sh{};
   if (sampled) {
-    uint64_t* slot = reinterpret_cast<uint64_t*>(w + p.off_slot);
-    const RowstatShape sh = rowstat_shape<T>(p.rows, V);
-    hipLaunchKernelGGL(k_zero_slots,
-                       dim3((unsigned)((p.rows * sh.Cb + kAccNT - 1) / kAccNT)), blk, 0, stream,
-                       slot, p.rows, sh.Cb, p.slot_stride, rowz);
+    sh = rowstat_shape<T>(p.rows, V);
     const int spin = g_rowstat_spin_limit.load(std::memory_order_relaxed);
 #define TV_ROWSTAT(E, PIPE)                                                                    \
   hipLaunchKernelGGL((k_rowstat<T, E, PIPE>), dim3(sh.grid), blk, 0, stream, target, draft, V, \
@@ -1169,7 +1178,8 @@ static void launch_accept_t(const AcceptPlan& p, const T* target, const T* draft
 #define TV_WALK(M)                                                                            \
   hipLaunchKernelGGL((k_walk<T, M>), dim3(batch), blk, 0, stream, target, draft, N, K, V, p.C, \
                      parent, token, depth, n_nodes, inv_t, seed, round, max_depth, cmax, carg, \
-                     cz, rowm, rowz, wtg, wqg, trows, p.rows, accept_len, accepted_nodes,     \
+                     cz, rowm, rowz, slot, p.slot_stride, sh.Cb, wtg, wqg, trows, p.rows,     \
+                     accept_len, accepted_nodes,                                              \
                      out_tokens, pend)
   if (!sampled) {
     TV_WALK(kGreedy);
