@@ -126,3 +126,23 @@ def test_ancestors(N):
         ga = host(g["anc"])[s].view(np.uint64)
         assert np.array_equal(ga[:n], anc)
         assert np.all(ga[n:] == 0)
+
+
+def test_build_workspace_reuse_and_many_rows():
+    """One workspace serves consecutive builds of one shape, whatever the
+    previous call left in it; 12 sequences x 16 positions of the full
+    vocabulary (228 draft rows' chunks per kernel launch)."""
+    c = workloads.CONFIGS["4b"]
+    b, K, V, k, B = 12, 16, c["V"], 8, 64
+    ws = torch.empty(tv.tree_build_workspace(b, K, V, k, B), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5)
+    for call in range(3):
+        r = np.random.default_rng(100 + call)
+        draft = (r.standard_normal((b, K, V)) * 3).astype(np.float32)
+        roots = r.integers(0, V, size=b).astype(np.int32)
+        ctx = r.integers(0, 5000, size=b).astype(np.int32)
+        g = tv.tv_tree_build(dev(draft), k, B, dev(roots), dev(ctx), workspace=ws)
+        torch.cuda.synchronize()
+        o = oracle.tree_build(draft, k, B, roots, ctx)
+        for s_ in range(b):
+            assert_tree_equal(g, o, s_)

@@ -12,7 +12,6 @@
 
 namespace {
 
-constexpr size_t kMaxSelectLds = 160 * 1024 - 1024;  // a workgroup's LDS, less the static part
 constexpr int kMaxGridY = 65535;
 
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
@@ -50,7 +49,7 @@ tv_status build_check(const void* draft_logits, tv_dtype dt, int batch, int K, i
   if (batch < 1 || K < 1 || V < 1 || topk < 1 || topk > V || budget < 0) return TV_ERR_INVALID;
   if (!build_args_ok(batch, K, V, topk, budget)) return TV_ERR_UNSUPPORTED;
   *plan = tvk::build_plan(batch, K, V, topk, budget);
-  if (plan->C * topk > 256 * tvk::kFinalizeE || plan->select_lds > kMaxSelectLds ||
+  if (plan->C * topk > 256 * tvk::kFinalizeE || plan->select_lds > tvk::kMaxSelectLds ||
       plan->rows > kMaxGridY)
     return TV_ERR_UNSUPPORTED;
   return TV_OK;

@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "tv_device.h"
 #include "tv_internal.h"
 
@@ -124,13 +126,11 @@ __device__ __forceinline__ void finalize_candidates(float (&val)[E], int (&id)[E
 // matter) and, once that add is performed, counts itself in rowrec[row][1];
 // the block that counts last has the whole mass Z and finalises the row
 // from the chunks' candidates (written by k_chunk_topk, one kernel before).
-// The chunk masses also go to cz[row][c].
 template <typename T>
 __global__ __launch_bounds__(kBuildNT) void k_chunk_z(const T* __restrict__ logits, int V,
                                                      int C, int chunk, int k, float inv_t,
                                                      const float* __restrict__ cval,
                                                      const int* __restrict__ cid,
-                                                     uint64_t* __restrict__ cz,
                                                      uint64_t* rowrec, int* __restrict__ ftok,
                                                      double* __restrict__ fq) {
   __shared__ TopkScratch<kBuildNT> sc;
@@ -172,7 +172,6 @@ __global__ __launch_bounds__(kBuildNT) void k_chunk_z(const T* __restrict__ logi
   if (threadIdx.x == 0) {
     uint64_t z = 0;
     for (int w = 0; w < kBuildNT / WAVE; ++w) z += wsum[w];
-    cz[row * C + c] = z;
     uint64_t* rec = rowrec + row * kRowRec;
     (void)__hip_atomic_fetch_add(&rec[0], z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // the add is performed before the count that announces it
@@ -784,7 +783,6 @@ BuildPlan build_plan(int batch, int K, int V, int topk, int budget) {
   };
   p.off_cval = take((size_t)p.rows * p.C * topk * sizeof(float));
   p.off_cid = take((size_t)p.rows * p.C * topk * sizeof(int));
-  p.off_cz = take((size_t)p.rows * p.C * sizeof(uint64_t));
   p.off_ftok = take((size_t)p.rows * topk * sizeof(int));
   p.off_fq = take((size_t)p.rows * topk * sizeof(double));
   p.off_rowrec = take((size_t)p.rows * kRowRec * sizeof(uint64_t));
@@ -798,7 +796,6 @@ static void launch_row_topk(const BuildPlan& p, const T* logits, int V, int k, f
                             char* w, hipStream_t stream) {
   float* cval = reinterpret_cast<float*>(w + p.off_cval);
   int* cid = reinterpret_cast<int*>(w + p.off_cid);
-  uint64_t* cz = reinterpret_cast<uint64_t*>(w + p.off_cz);
   int* ftok = reinterpret_cast<int*>(w + p.off_ftok);
   double* fq = reinterpret_cast<double*>(w + p.off_fq);
   uint64_t* rowrec = reinterpret_cast<uint64_t*>(w + p.off_rowrec);
@@ -807,7 +804,26 @@ static void launch_row_topk(const BuildPlan& p, const T* logits, int V, int k, f
   hipLaunchKernelGGL((k_chunk_topk<T, E1>), g1, dim3(kBuildNT), 0, stream, logits, V, p.C,
                      p.chunk, k, cval, cid, rowrec);
   hipLaunchKernelGGL((k_chunk_z<T>), g1, dim3(kBuildNT), 0, stream, logits, V, p.C, p.chunk, k,
-                     inv_t, cval, cid, cz, rowrec, ftok, fq);
+                     inv_t, cval, cid, rowrec, ftok, fq);
+}
+
+// The selection's lists live in dynamic LDS, beyond 64 KB for large budgets
+// (gfx950 gives a workgroup up to 160 KB once the kernel allows it): the
+// limit is raised once per device and kernel, to the largest the host's
+// checks admit (kMaxSelectLds), outside the per-call path.
+template <int NT>
+static hipError_t allow_select_lds(size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  static std::atomic<int> done[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::atomic<int>& flag = done[dev & 63];
+  if (flag.load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_select<NT>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxSelectLds);
+  if (e == hipSuccess) flag.store(1, std::memory_order_release);
+  return e;
 }
 
 hipError_t launch_build(const BuildPlan& p, const void* draft, bool bf16, int batch, int K,
@@ -825,16 +841,10 @@ hipError_t launch_build(const BuildPlan& p, const void* draft, bool bf16, int ba
   // one workgroup per sequence; larger budgets have longer candidate lists,
   // whose counting passes gain from more waves (measured: 256 threads up to
   // budget 127, 512 up to 511, then 1024)
-  // the selection's lists live in dynamic LDS, beyond 64 KB for large
-  // budgets (gfx950 gives a workgroup up to 160 KB once the kernel allows it)
 #define TV_SELECT(NT)                                                                          \
   do {                                                                                         \
-    if (p.select_lds > 65536) {                                                                \
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_select<NT>),   \
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,     \
-                                               (int)p.select_lds);                             \
-      if (e != hipSuccess) return e;                                                           \
-    }                                                                                          \
+    const hipError_t e = allow_select_lds<NT>(p.select_lds);                                   \
+    if (e != hipSuccess) return e;                                                             \
     hipLaunchKernelGGL((k_select<NT>), dim3(batch), dim3(NT), p.select_lds, stream, ftok, fq,  \
                        K, topk, budget, p.P, root_token, ctx_len, parent, token, depth, pos,    \
                        score, anc, n_nodes);                                                   \

@@ -16,13 +16,14 @@ namespace tvk {
 constexpr int kBuildChunk = 8192;  // tokens per block in the draft-row passes
 constexpr int kRankMax = 512;  // depth lists up to this size are ordered by rank counting
 constexpr int kFinalizeE = 8;      // per-thread items when merging chunk candidates
+constexpr size_t kMaxSelectLds = 160 * 1024 - 1024;  // the selection's dynamic LDS, at most
 
 struct BuildPlan {
   int chunk, C;
   int64_t rows;
   int P;  // LDS room for the candidates of one depth (a power of two)
   size_t select_lds;
-  size_t off_cval, off_cid, off_cz, off_ftok, off_fq;
+  size_t off_cval, off_cid, off_ftok, off_fq;
   size_t off_rowrec;  // per-row mass accumulator and arrival count (256-byte lines)
   size_t workspace;
 };
