@@ -29,9 +29,9 @@ verified per second (rounds/s x N x Hq); config.batch_ms splits the timed
 steps into five equal batches (median beside the mean).  `roofline` is for
 the dominant kernel of the verification pass, k_attn_partial: its
 algorithmic bytes (every input of the call read once) or the call's flops
-over its own duration, from HIP events on the call's stream -- one recorded
-before the call and one that the library records between the partial and
-combine kernels (its timing hook) -- with the whole call's figures in
+over its own duration, from HIP events on the call's stream that the
+library records just before the partial kernel and between it and the
+combine (its timing hook), with the whole call's figures in
 roofline.call.  Its `traffic` comes from the HBM byte counters recorded in
 profiles/attention_<workload>_traffic.md when that record was taken on the
 current attention source (else null).  per_call.attention_8b is the
@@ -274,22 +274,24 @@ def attention_8b(dev, stream, rotate_gib=1.0, reps=100):
                      dtype=torch.uint8, device=dev)
     out = torch.empty((b, N, c["Hq"], c["D"]), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((b, N, c["Hq"]), dtype=torch.float32, device=dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
     for e in evs:
         e[1].record(stream)
+        e[3].record(stream)
     for i in range(reps + 5):
         q, k, v = sets[i % nsets]
         if i >= 5:
             evs[i - 5][0].record(stream)
-            tv.lib().tv_debug_set_attention_event(evs[i - 5][1].cuda_event)
+            tv.lib().tv_debug_set_attention_events(evs[i - 5][3].cuda_event,
+                                                   evs[i - 5][1].cuda_event)
         tv.tv_tree_attention_verify(q, k, v, ctx, tree["anc"], tree["n_nodes"], L, workspace=ws,
                                     out=out, lse=lse)
         if i >= 5:
-            tv.lib().tv_debug_set_attention_event(None)
+            tv.lib().tv_debug_set_attention_events(None, None)
             evs[i - 5][2].record(stream)
     torch.cuda.synchronize()
     call = sum(e[0].elapsed_time(e[2]) for e in evs) / reps
-    part = sum(e[0].elapsed_time(e[1]) for e in evs) / reps
+    part = sum(e[3].elapsed_time(e[1]) for e in evs) / reps
     comb = sum(e[1].elapsed_time(e[2]) for e in evs) / reps
     flops = attention_flops(c, tree["n_nodes"].cpu().numpy(), tree["depth"].cpu().numpy(),
                             ctx.cpu().numpy())
@@ -406,12 +408,12 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         if ev is not None and bf:
-            tv.lib().tv_debug_set_attention_event(ev[4].cuda_event)
+            tv.lib().tv_debug_set_attention_events(ev[5].cuda_event, ev[4].cuda_event)
         tv.tv_tree_attention_verify(s["q"], s["k"], s["v"], s["ctx"], tree["anc"], tree["n_nodes"],
                                     max_ctx, workspace=ws_a, out=attn_out, lse=lse)
         if ev is not None:
             if bf:
-                tv.lib().tv_debug_set_attention_event(None)
+                tv.lib().tv_debug_set_attention_events(None, None)
             ev[2].record(stream)
         tv.tv_tree_accept(s["target"], tree["parent"], tree["token"], tree["depth"], tree["n_nodes"],
                           mode=mode, temperature=max(args.temperature, 1e-3), seed=1234, round=step,
@@ -479,12 +481,14 @@ def main():
     # the stream the calls run on (events cannot be recorded inside a graph
     # on this platform): the per-call times and the roofline come from here
     # evs[i]: before build, after build, after attention, after accept, and
-    # (bf16) between the attention's partial and combine kernels, recorded by
-    # the library through its timing hook; each event is recorded once here
-    # so that it exists before its handle is passed on
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # (bf16) between the attention's partial and combine kernels and just
+    # before the partial kernel, the last two recorded by the library through
+    # its timing hook; each event is recorded once here so that it exists
+    # before its handle is passed on
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for e in evs:
         e[4].record(stream)
+        e[5].record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
@@ -500,9 +504,9 @@ def main():
         calls[name] = sum(evs[i][a].elapsed_time(evs[i][z]) for i in range(args.steps)) / args.steps
     kern = {}
     if bf:
-        # event to event on the call's stream: the partial kernel (from the
-        # event before the call) and the combine (to the event after it)
-        kern["k_attn_partial"] = sum(evs[i][1].elapsed_time(evs[i][4])
+        # event to event on the call's stream: the partial kernel (between the
+        # library's two events) and the combine (to the event after the call)
+        kern["k_attn_partial"] = sum(evs[i][5].elapsed_time(evs[i][4])
                                      for i in range(args.steps)) / args.steps
         kern["k_attn_combine"] = sum(evs[i][4].elapsed_time(evs[i][2])
                                      for i in range(args.steps)) / args.steps

@@ -31,7 +31,7 @@
  *     share that GPU's scratch buffer; for
  *     large budgets tv_tree_build raises its selection kernel's dynamic-LDS
  *     limit in the HIP runtime, an idempotent setting; the test hooks
- *     tv_debug_set_spin_limit and tv_debug_set_attention_event change
+ *     tv_debug_set_spin_limit and tv_debug_set_attention_events change
  *     process-wide settings).
  *   - Arguments are checked on the host before any launch; a bad argument
  *     returns TV_ERR_INVALID (or TV_ERR_UNSUPPORTED for a valid request this
@@ -114,13 +114,14 @@ int tv_version(void);
  * gives the same results.  Process-wide; returns the previous value. */
 int tv_debug_set_spin_limit(int polls);
 
-/* Test hook for timing: when `ev` is not null, every later bf16
- * tv_tree_attention_verify(_rope) call records `ev` on its stream between
- * its two kernels (the split partials and their combine), so that events
- * recorded by the caller before and after the call bracket each kernel.
- * null (the default) records nothing.  Process-wide; the caller keeps `ev`
- * valid while it is set.  Returns TV_OK. */
-tv_status tv_debug_set_attention_event(hipEvent_t ev);
+/* Test hook for timing: every later bf16 tv_tree_attention_verify(_rope)
+ * call records `before` on its stream just before its first kernel (the
+ * split partials) and `between` between that kernel and the second (their
+ * combine), each when not null, so that with one more event recorded by the
+ * caller after the call the two kernels are bracketed one by one.  null
+ * (the default) records nothing.  Process-wide; the caller keeps the events
+ * valid while they are set.  Returns TV_OK. */
+tv_status tv_debug_set_attention_events(hipEvent_t before, hipEvent_t between);
 
 /* Test hook: the fixed-point softmax weight that the builder and the
  * acceptance kernels give a logit (the primer's "acceptance and rejection":

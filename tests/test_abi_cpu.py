@@ -328,4 +328,4 @@ def test_debug_hooks_reject_on_host():
     assert L.tv_debug_weights(0, 16, float("inf"), 1.0, 0, FAKE, None) == tv.TV_ERR_INVALID
     assert L.tv_debug_weights(0, 16, 0.0, 0.0, 0, FAKE, None) == tv.TV_ERR_INVALID
     assert L.tv_debug_weights(0, 16, 0.0, 0.7, 1, FAKE, None) == tv.TV_ERR_INVALID
-    assert L.tv_debug_set_attention_event(None) == tv.TV_OK
+    assert L.tv_debug_set_attention_events(None, None) == tv.TV_OK

@@ -40,7 +40,7 @@ EXPORTS = ("tv_status_string", "tv_version", "tv_tree_build_workspace", "tv_tree
            "tv_tree_accept_workspace", "tv_tree_accept", "tv_tree_budget", "tv_kv_commit",
            "tv_tree_root", "tv_tree_expand_workspace", "tv_tree_expand",
            "tv_tree_attention_verify_rope", "tv_kv_commit_rope", "tv_tree_check",
-           "tv_debug_set_spin_limit", "tv_tree_build_noalloc", "tv_debug_set_attention_event",
+           "tv_debug_set_spin_limit", "tv_tree_build_noalloc", "tv_debug_set_attention_events",
            "tv_debug_weights")
 
 _lib = None
@@ -76,8 +76,8 @@ def _load():
     L.tv_tree_build.restype = i32
     L.tv_debug_weights.argtypes = [c.c_uint32, c.c_uint32, f32, f32, i32, vp, vp]
     L.tv_debug_weights.restype = i32
-    L.tv_debug_set_attention_event.argtypes = [vp]
-    L.tv_debug_set_attention_event.restype = i32
+    L.tv_debug_set_attention_events.argtypes = [vp, vp]
+    L.tv_debug_set_attention_events.restype = i32
     L.tv_tree_build_noalloc.argtypes = [vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp,
                                         vp, vp, vp, vp, vp]
     L.tv_tree_build_noalloc.restype = i32

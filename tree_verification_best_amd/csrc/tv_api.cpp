@@ -357,8 +357,8 @@ tv_status tv_debug_weights(uint32_t first_bits, uint32_t count, float row_max, f
       tvk::launch_debug_weights(first_bits, count, row_max, inv_t, unit != 0, out, stream));
 }
 
-tv_status tv_debug_set_attention_event(hipEvent_t ev) {
-  tvk::set_attention_mid_event(ev);
+tv_status tv_debug_set_attention_events(hipEvent_t before, hipEvent_t between) {
+  tvk::set_attention_events(before, between);
   return TV_OK;
 }
 

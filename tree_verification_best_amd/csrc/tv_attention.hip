@@ -776,10 +776,13 @@ AttnPlan attention_plan(int batch, int N, int Hq, int Hkv, int D, int max_ctx, i
 }
 
 namespace {
-std::atomic<hipEvent_t> g_mid_event{nullptr};
+std::atomic<hipEvent_t> g_pre_event{nullptr}, g_mid_event{nullptr};
 }  // namespace
 
-hipEvent_t set_attention_mid_event(hipEvent_t ev) { return g_mid_event.exchange(ev); }
+void set_attention_events(hipEvent_t before, hipEvent_t between) {
+  g_pre_event.store(before);
+  g_mid_event.store(between);
+}
 
 hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, const void* v,
                             bool bf16, const int* ctx_len, const uint64_t* anc,
@@ -814,6 +817,10 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, con
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
+  if (hipEvent_t ev = g_pre_event.load(std::memory_order_relaxed)) {
+    const hipError_t e = hipEventRecord(ev, stream);
+    if (e != hipSuccess) return e;
+  }
 #define TV_PARTIAL(DD, R)                                                                   \
   hipLaunchKernelGGL((k_attn_partial<DD, R>), dim3(grid), dim3(kAttnThreads), 0, stream, q16, \
                      k16, v16, ctx_len, anc, n_nodes, N, Hq, Hkv, cap, p.splits,              \

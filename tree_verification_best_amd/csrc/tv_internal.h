@@ -63,9 +63,9 @@ struct AttnPlan {
 };
 
 AttnPlan attention_plan(int batch, int N, int Hq, int Hkv, int D, int max_ctx, int splits);
-// Timing hook: an event recorded between the partial and combine kernels
-// (nullptr: none).  Returns the previous one.
-hipEvent_t set_attention_mid_event(hipEvent_t ev);
+// Timing hook: events recorded just before the partial kernel and between
+// the partial and combine kernels (nullptr: none).
+void set_attention_events(hipEvent_t before, hipEvent_t between);
 hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, const void* v,
                             bool bf16, const int* ctx_len, const uint64_t* anc,
                             const int* n_nodes, int batch, int N, int Hq, int Hkv, int D,
