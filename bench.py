@@ -274,23 +274,34 @@ def attention_8b(dev, stream, rotate_gib=1.0, reps=100):
                      dtype=torch.uint8, device=dev)
     out = torch.empty((b, N, c["Hq"], c["D"]), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((b, N, c["Hq"]), dtype=torch.float32, device=dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
-    for e in evs:
-        e[1].record(stream)
-        e[3].record(stream)
-    for i in range(reps + 5):
-        q, k, v = sets[i % nsets]
-        if i >= 5:
-            evs[i - 5][0].record(stream)
-            tv.lib().tv_debug_set_attention_events(evs[i - 5][3].cuda_event,
-                                                   evs[i - 5][1].cuda_event)
-        tv.tv_tree_attention_verify(q, k, v, ctx, tree["anc"], tree["n_nodes"], L, workspace=ws,
-                                    out=out, lse=lse)
-        if i >= 5:
-            tv.lib().tv_debug_set_attention_events(None, None)
-            evs[i - 5][2].record(stream)
-    torch.cuda.synchronize()
+
+    def timed(hook):
+        # hook: the library also records events just before the partial
+        # kernel and between the two kernels (extra markers; see above)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+        for e in evs:
+            e[1].record(stream)
+            e[3].record(stream)
+        torch.cuda.synchronize()
+        for i in range(reps + 5):
+            q, k, v = sets[i % nsets]
+            if i >= 5:
+                evs[i - 5][0].record(stream)
+                if hook:
+                    tv.lib().tv_debug_set_attention_events(evs[i - 5][3].cuda_event,
+                                                           evs[i - 5][1].cuda_event)
+            tv.tv_tree_attention_verify(q, k, v, ctx, tree["anc"], tree["n_nodes"], L,
+                                        workspace=ws, out=out, lse=lse)
+            if i >= 5:
+                if hook:
+                    tv.lib().tv_debug_set_attention_events(None, None)
+                evs[i - 5][2].record(stream)
+        torch.cuda.synchronize()
+        return evs
+
+    evs = timed(False)
     call = sum(e[0].elapsed_time(e[2]) for e in evs) / reps
+    evs = timed(True)
     part = sum(e[3].elapsed_time(e[1]) for e in evs) / reps
     comb = sum(e[1].elapsed_time(e[2]) for e in evs) / reps
     flops = attention_flops(c, tree["n_nodes"].cpu().numpy(), tree["depth"].cpu().numpy(),
@@ -396,7 +407,7 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
 
-    def round_(step, ev=None):
+    def round_(step, ev=None, hk=None):
         s = sets[step % nsets]
         if ev is not None:
             ev[0].record(stream)
@@ -407,13 +418,13 @@ def main():
                                  out=dict(depth=tree["depth"], pos=tree["pos"], anc=tree["anc"]))
         if ev is not None:
             ev[1].record(stream)
-        if ev is not None and bf:
-            tv.lib().tv_debug_set_attention_events(ev[5].cuda_event, ev[4].cuda_event)
+        if hk is not None:
+            tv.lib().tv_debug_set_attention_events(hk[0].cuda_event, hk[1].cuda_event)
         tv.tv_tree_attention_verify(s["q"], s["k"], s["v"], s["ctx"], tree["anc"], tree["n_nodes"],
                                     max_ctx, workspace=ws_a, out=attn_out, lse=lse)
+        if hk is not None:
+            tv.lib().tv_debug_set_attention_events(None, None)
         if ev is not None:
-            if bf:
-                tv.lib().tv_debug_set_attention_events(None, None)
             ev[2].record(stream)
         tv.tv_tree_accept(s["target"], tree["parent"], tree["token"], tree["depth"], tree["n_nodes"],
                           mode=mode, temperature=max(args.temperature, 1e-3), seed=1234, round=step,
@@ -432,10 +443,11 @@ def main():
     # step's last event, so outside the per-call brackets)
     acc_sum = torch.zeros((b,), dtype=torch.int64, device=dev)
 
-    def eager_steps(first, n, evs=None):
+    def eager_steps(first, n, evs=None, hks=None):
         for i in range(n):
-            round_(first + i, evs[i] if evs is not None else None)
-            if evs is not None:
+            round_(first + i, evs[i] if evs is not None else None,
+                   hks[i] if hks is not None else None)
+            if evs is not None and hks is None:
                 acc_sum.add_(acc["accept_len"])
 
     for i in range(args.warmup):
@@ -480,15 +492,8 @@ def main():
     # eager launches of the same steps with HIP events around every call on
     # the stream the calls run on (events cannot be recorded inside a graph
     # on this platform): the per-call times and the roofline come from here
-    # evs[i]: before build, after build, after attention, after accept, and
-    # (bf16) between the attention's partial and combine kernels and just
-    # before the partial kernel, the last two recorded by the library through
-    # its timing hook; each event is recorded once here so that it exists
-    # before its handle is passed on
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    for e in evs:
-        e[4].record(stream)
-        e[5].record(stream)
+    # evs[i]: before build, after build, after attention, after accept
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
@@ -504,11 +509,24 @@ def main():
         calls[name] = sum(evs[i][a].elapsed_time(evs[i][z]) for i in range(args.steps)) / args.steps
     kern = {}
     if bf:
-        # event to event on the call's stream: the partial kernel (between the
-        # library's two events) and the combine (to the event after the call)
-        kern["k_attn_partial"] = sum(evs[i][5].elapsed_time(evs[i][4])
+        # a second eager pass of the same steps in which the library records
+        # an event just before the partial kernel and one between it and the
+        # combine (its timing hook; every event recorded once beforehand so
+        # that it exists before its handle is passed on): the partial kernel
+        # is timed between those two, the combine to the event after the
+        # call.  The extra markers lengthen the call, so the per-call times
+        # above come from the pass without them.
+        hks = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        evs2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for h in hks:
+            h[0].record(stream)
+            h[1].record(stream)
+        torch.cuda.synchronize()
+        eager_steps(args.warmup, args.steps, evs2, hks)
+        torch.cuda.synchronize()
+        kern["k_attn_partial"] = sum(hks[i][0].elapsed_time(hks[i][1])
                                      for i in range(args.steps)) / args.steps
-        kern["k_attn_combine"] = sum(evs[i][4].elapsed_time(evs[i][2])
+        kern["k_attn_combine"] = sum(hks[i][1].elapsed_time(evs2[i][2])
                                      for i in range(args.steps)) / args.steps
     mean_accept = float(acc_sum.sum().item()) / (args.steps * b)
     sweep = {}
@@ -682,7 +700,9 @@ def main():
                 "algorithmic_flops": aflops,
                 "intensity_flop_per_byte": round(intensity, 1)}
         if bf:
-            # both kernels, without the gaps between and around them
+            # the two kernels' bracketed times added: the partial between the
+            # library's events, the combine from there to the event after the
+            # call (the gap before the call left out)
             pair = kern["k_attn_partial"] + kern["k_attn_combine"]
             roof["call"]["kernels_frac"] = fig(abytes["attention"], pair)[1]
 
