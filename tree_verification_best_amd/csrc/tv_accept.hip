@@ -239,9 +239,12 @@ __device__ __forceinline__ void chunk_mass(const float (&x)[E], const T* p, int 
 // deep: the next row's span is loaded during the wait and posted before the
 // current span is weighed.
 //
-// Slots: slot[r * slot_stride + cb] = 2^32 | bits of the span maximum, an
-// agent-scope atomic store; a reader's wave polls the row's Cb slots with
-// agent-scope atomic loads until every one is posted.  One store and one
+// Slots: slot[r * slot_stride + cb] = tag << 32 | bits of the span maximum,
+// an agent-scope atomic store; a reader's wave polls the row's Cb slots with
+// agent-scope atomic loads until every one carries this call's tag.  The tag
+// is 2 * generation + 1, the generation a word of the workspace that the
+// walk advances once per call, so slots never need clearing: a slot holds
+// zero (a new workspace) or the previous call's tag until it is posted.  One store and one
 // load per hand-off, no cache-wide maintenance.  The maxima of the 4096-token
 // chunks also go to cmax[c][r] for the walk.
 //
@@ -250,15 +253,15 @@ __device__ __forceinline__ void chunk_mass(const float (&x)[E], const T* p, int 
 // the same: a block that has polled spin_limit times in vain (other work
 // holding the device, say) takes the row maximum from the whole row itself,
 // which gives the same value, so the results never depend on the schedule.
-// The slots and the rows' mass accumulators must be zero at the start: a
-// new workspace is zero-filled by its owner, and k_walk, the call's last
-// reader of them, returns them to zero (so no clearing launch is needed and
-// replays of a captured call find them as the first call did).  Each row's
-// slots start on a 256-byte line of their own.
+// The rows' mass accumulators must be zero at the start: a new workspace is
+// zero-filled by its owner, and k_walk, their last reader, returns them to
+// zero (so no clearing launch is needed and replays of a captured call find
+// them as the first call did).  Each row's slots start on a 256-byte line of
+// their own, and each row's mass on another.
 template <int E>
 __device__ __forceinline__ void post_span_max(const float (&x)[E], float* sv, float* cmax,
                                               uint64_t* slot, int C, int cb, int64_t r,
-                                              int64_t rows, int slot_stride) {
+                                              int64_t rows, int slot_stride, uint32_t tag) {
   float bv = x[0];
 #pragma unroll
   for (int j = 1; j < E; ++j) bv = fmaxf(bv, x[j]);
@@ -275,7 +278,7 @@ __device__ __forceinline__ void post_span_max(const float (&x)[E], float* sv, fl
       if (c < C) cmax[(int64_t)c * rows + r] = ck;
       all = fmaxf(all, ck);
     }
-    const uint64_t v = (1ull << 32) | __builtin_bit_cast(uint32_t, all);
+    const uint64_t v = ((uint64_t)tag << 32) | __builtin_bit_cast(uint32_t, all);
     __hip_atomic_store(&slot[r * slot_stride + cb], v, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -296,6 +299,7 @@ __global__ __launch_bounds__(kAccNT) void k_rowstat(const T* __restrict__ target
                                                    const int* __restrict__ n_nodes,
                                                    uint64_t* __restrict__ wtg,
                                                    uint64_t* __restrict__ wqg,
+                                                   const uint32_t* __restrict__ gen,
                                                    int spin_limit) {
   __shared__ float sv[kAccNT / WAVE];
   __shared__ float sl[kAccNT / WAVE];
@@ -308,9 +312,12 @@ __global__ __launch_bounds__(kAccNT) void k_rowstat(const T* __restrict__ target
   const int lane = lane_id();
   int64_t r = blockIdx.x / (unsigned)Cb;
   if (r >= rows) return;
+  // this call's slot tag: odd, so never the zero of a new workspace, and
+  // different from the previous call's (the walk advances the generation)
+  const uint32_t tag = (gen[0] << 1) | 1u;
   float x[E];
   ChunkLoad<T>::load(row_ptr(target, draft, r, trows, V), cb * kSpan, V, x);
-  post_span_max(x, sv, cmax, slot, C, cb, r, rows, slot_stride);
+  post_span_max(x, sv, cmax, slot, C, cb, r, rows, slot_stride, tag);
   for (; r < rows; r += J) {
     const T* p = row_ptr(target, draft, r, trows, V);
     const int64_t rn = r + J;
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(kAccNT) void k_rowstat(const T* __restrict__ target
       int late = 0, spins = 0;
       while (true) {
         v = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (__all((v >> 32) != 0)) break;
+        if (__all((uint32_t)(v >> 32) == tag)) break;
         if (spins >= spin_limit) {
           late = 1;
           break;
@@ -352,7 +359,7 @@ __global__ __launch_bounds__(kAccNT) void k_rowstat(const T* __restrict__ target
       for (int w = 1; w < kAccNT / WAVE; ++w) m = fmaxf(m, sl[w]);
     }
     if constexpr (PIPE) {
-      if (rn < rows) post_span_max(y, sv, cmax, slot, C, cb, rn, rows, slot_stride);
+      if (rn < rows) post_span_max(y, sv, cmax, slot, C, cb, rn, rows, slot_stride, tag);
     }
     chunk_mass<T, E>(x, p, V, C, cb, r, trows, rows, m, inv_t, wsum, cz, N, K, parent, token,
                      depth, n_nodes, wtg, wqg);
@@ -373,7 +380,7 @@ __global__ __launch_bounds__(kAccNT) void k_rowstat(const T* __restrict__ target
         for (int j = 0; j < E; ++j) x[j] = y[j];
       } else {
         ChunkLoad<T>::load(row_ptr(target, draft, rn, trows, V), cb * kSpan, V, x);
-        post_span_max(x, sv, cmax, slot, C, cb, rn, rows, slot_stride);
+        post_span_max(x, sv, cmax, slot, C, cb, rn, rows, slot_stride, tag);
       }
     }
   }
@@ -508,7 +515,7 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
     const int* __restrict__ depth, const int* __restrict__ n_nodes, float inv_t,
     uint64_t seed, uint64_t round, int max_depth, const float* __restrict__ cmax,
     const int* __restrict__ carg, const uint64_t* __restrict__ cz,
-    const float* __restrict__ rowm, uint64_t* rowz, uint64_t* slot, int slot_stride, int Cb,
+    const float* __restrict__ rowm, uint64_t* rowz, uint32_t* gen,
     const uint64_t* __restrict__ wtg, const uint64_t* __restrict__ wqg, int64_t trows,
     int64_t rows, int* __restrict__ accept_len, int* __restrict__ accepted_nodes,
     int* __restrict__ out_tokens, DraftPending* __restrict__ pend) {
@@ -578,16 +585,16 @@ __global__ __launch_bounds__(kAccNT) void k_walk(
       tmv[k] = rowm[grow];
       tzv[k] = rowz[grow * kRowzStride];
     }
-    // the row pass's hand-off state of this sequence's rows goes back to
-    // zero for the next call (each thread clears what it has just read; the
-    // spans' slots are not read after the row pass)
+    // the rows' mass accumulators go back to zero for the next call (each
+    // thread clears what it has just read), and the next call's row pass
+    // tags its slots anew (every row pass of this call has ended)
+    if (b == 0 && tid == 0) gen[0] = gen[0] + 1u;
 #pragma unroll
     for (int k = 0; k < kRowsPer; ++k) {
       const int r = tid + k * kAccNT;
       if (r < nr) {
         const int64_t grow = r < N ? rb + r : trows + (int64_t)b * K + (r - N);
         rowz[grow * kRowzStride] = 0;
-        for (int c = 0; c < Cb; ++c) slot[grow * slot_stride + c] = 0;
       }
     }
   } else {
@@ -1058,6 +1065,7 @@ AcceptPlan accept_plan(int batch, int N, int K, int V, bool sampled, bool draft)
   p.off_slot = sampled ? take((size_t)p.rows * p.slot_stride * sizeof(uint64_t)) : 0;
   p.off_rowz = sampled ? take((size_t)p.rows * kRowzStride * sizeof(uint64_t)) : 0;
   p.off_rowm = sampled ? take((size_t)p.rows * sizeof(float)) : 0;
+  p.off_gen = sampled ? take(sizeof(uint32_t)) : 0;  // the slots' generation
   p.workspace = off;
   return p;
 }
@@ -1153,6 +1161,7 @@ static void launch_accept_t(const AcceptPlan& p, const T* target, const T* draft
   uint64_t* rowz = sampled ? reinterpret_cast<uint64_t*>(w + p.off_rowz) : nullptr;
   float* rowm = sampled ? reinterpret_cast<float*>(w + p.off_rowm) : nullptr;
   uint64_t* slot = sampled ? reinterpret_cast<uint64_t*>(w + p.off_slot) : nullptr;
+  uint32_t* gen = sampled ? reinterpret_cast<uint32_t*>(w + p.off_gen) : nullptr;
   const int64_t trows = (int64_t)batch * N;
   const dim3 g(p.C, (unsigned)p.rows);
   const dim3 blk(kAccNT);
@@ -1163,7 +1172,7 @@ static void launch_accept_t(const AcceptPlan& p, const T* target, const T* draft
 #define TV_ROWSTAT(E, PIPE)                                                                    \
   hipLaunchKernelGGL((k_rowstat<T, E, PIPE>), dim3(sh.grid), blk, 0, stream, target, draft, V, \
                      p.C, sh.Cb, trows, p.rows, inv_t, cmax, slot, p.slot_stride, cz, rowm,    \
-                     rowz, N, K, parent, token, depth, n_nodes, wtg, wqg, spin)
+                     rowz, N, K, parent, token, depth, n_nodes, wtg, wqg, gen, spin)
     if (sh.E == 32)
       TV_ROWSTAT(32, false);
     else if (!sh.pipe)
@@ -1178,8 +1187,7 @@ static void launch_accept_t(const AcceptPlan& p, const T* target, const T* draft
 #define TV_WALK(M)                                                                            \
   hipLaunchKernelGGL((k_walk<T, M>), dim3(batch), blk, 0, stream, target, draft, N, K, V, p.C, \
                      parent, token, depth, n_nodes, inv_t, seed, round, max_depth, cmax, carg, \
-                     cz, rowm, rowz, slot, p.slot_stride, sh.Cb, wtg, wqg, trows, p.rows,     \
-                     accept_len, accepted_nodes,                                              \
+                     cz, rowm, rowz, gen, wtg, wqg, trows, p.rows, accept_len, accepted_nodes, \
                      out_tokens, pend)
   if (!sampled) {
     TV_WALK(kGreedy);

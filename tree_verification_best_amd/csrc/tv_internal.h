@@ -87,6 +87,7 @@ struct AcceptPlan {
   size_t off_slot;   // per-row slots of the chunk maxima, one-pass statistics (sampled)
   int slot_stride;   // slots per row (256-byte rows)
   size_t off_rowz, off_rowm;  // sampled: every row's mass Z and maximum, for the walk
+  size_t off_gen;             // sampled: the row pass's slot generation
   size_t workspace;
 };
 
