@@ -39,6 +39,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "tv_device.h"
 #include "tv_internal.h"
@@ -181,20 +182,34 @@ __global__ __launch_bounds__(kBuildNT) void k_chunk_z(const T* __restrict__ logi
   }
   __syncthreads();
   if (!s_last) return;
-  // the row's last block: the whole mass is in the accumulator
+  // the row's last block: the whole mass is in the accumulator.  The C * k
+  // candidates take the fewest items per thread that hold them (152 at the
+  // 4B shape: one), since every item costs the block top-k its work.
   const int n = C * k;
-  float val[kFinalizeE];
-  int id[kFinalizeE];
-#pragma unroll
-  for (int e = 0; e < kFinalizeE; ++e) {
-    const int j = e * kBuildNT + (int)threadIdx.x;
-    const bool ok = j < n;
-    val[e] = ok ? cval[row * n + j] : -__builtin_inff();
-    id[e] = ok ? cid[row * n + j] : V + C * chunk + j;
-  }
   const uint64_t Z =
       __hip_atomic_load(&rowrec[row * kRowRec], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  finalize_candidates<kFinalizeE>(val, id, Z, V, k, inv_t, sc, tv, ti, tq, ftok, fq, row);
+  auto finalize = [&](auto Ec) {
+    constexpr int FE = decltype(Ec)::value;
+    float val[FE];
+    int id[FE];
+#pragma unroll
+    for (int e = 0; e < FE; ++e) {
+      const int j = e * kBuildNT + (int)threadIdx.x;
+      const bool ok = j < n;
+      val[e] = ok ? cval[row * n + j] : -__builtin_inff();
+      id[e] = ok ? cid[row * n + j] : V + C * chunk + j;
+    }
+    finalize_candidates<FE>(val, id, Z, V, k, inv_t, sc, tv, ti, tq, ftok, fq, row);
+  };
+  static_assert(kFinalizeE == 8, "the cases below cover up to 8 items per thread");
+  if (n <= kBuildNT)
+    finalize(std::integral_constant<int, 1>());
+  else if (n <= 2 * kBuildNT)
+    finalize(std::integral_constant<int, 2>());
+  else if (n <= 4 * kBuildNT)
+    finalize(std::integral_constant<int, 4>());
+  else
+    finalize(std::integral_constant<int, 8>());
 }
 
 // ---------------------------------------------------------------------------
