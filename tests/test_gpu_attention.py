@@ -10,7 +10,7 @@ import torch
 import oracle
 import tree_verification_best_amd as tv
 import workloads
-from gpu_util import assert_attention_close, bf16_dev, dev
+from gpu_util import assert_attention_close, bf16_dev, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -163,3 +163,35 @@ def test_attention_bf16_output_is_rounded_fp32():
     assert o16.dtype == torch.bfloat16
     assert torch.equal(o16, o32.to(torch.bfloat16))
     assert torch.equal(l16, l32)
+
+
+@pytest.mark.parametrize("splits,D,dt", [(0, 128, "bf16"), (1, 128, "bf16"), (3, 128, "bf16"),
+                                         (7, 128, "bf16"), (3, 64, "bf16"), (0, 128, "f32")])
+def test_attention_unread_rows_hold_nan_and_inf(splits, D, dt):
+    """Cache rows no node can see (past each sequence's context plus its
+    tree nodes) hold NaN and +-Inf: the result must not change.  The short
+    and ragged contexts make the first tile of some context splits end
+    early, the case where the kernel loads rows past the end."""
+    r = np.random.default_rng(100 + splits + D)
+    b, N, Hq, Hkv = 4, 33, 8, 2
+    Ls, ns = [100, 300, 0, 1000], [10, 16, 5, 33]
+    cap = max(Ls) + N + 150
+    rnd = workloads.round_bf16 if dt == "bf16" else (lambda x: x)
+    q = rnd(r.standard_normal((b, N, Hq, D)).astype(np.float32))
+    k = rnd(r.standard_normal((b, Hkv, cap, D)).astype(np.float32))
+    v = rnd(r.standard_normal((b, Hkv, cap, D)).astype(np.float32))
+    bad = np.array([np.nan, np.inf, -np.inf], np.float32)
+    for s in range(b):
+        tail = cap - (Ls[s] + ns[s])
+        k[s, :, Ls[s] + ns[s]:, :] = bad[r.integers(0, 3, (Hkv, tail, D))]
+        v[s, :, Ls[s] + ns[s]:, :] = bad[r.integers(0, 3, (Hkv, tail, D))]
+    anc = np.stack([_tree(r, "random", ns[s], N)[1] for s in range(b)])
+    ctx, nn = np.array(Ls, np.int32), np.array(ns, np.int32)
+    put = bf16_dev if dt == "bf16" else dev
+    out, lse = tv.tv_tree_attention_verify(put(q), put(k), put(v), dev(ctx),
+                                           dev(anc.view(np.int64)), dev(nn), max(Ls),
+                                           splits=splits)
+    torch.cuda.synchronize()
+    ro, rl = oracle.tree_attention(q, k, v, ctx, anc, nn)
+    assert np.all(np.isfinite(host(out).astype(np.float64)[:, :]))
+    assert_attention_close(out, lse, ro, rl, nn, f"unread rows, splits {splits}, D {D}, {dt}")

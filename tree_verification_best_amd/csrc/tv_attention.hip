@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
 #pragma unroll
         for (int i = 0; i < KLD; i += 2) {
           const int t = kt - L + ckey[i];
-          const int kp = t < n ? Pk[t] : 0;  // rows past the end stage as zeros
+          const int kp = t < n ? Pk[t] : 0;  // rows past the end: position 0 (masked)
           bf16x8 lo = __builtin_bit_cast(bf16x8, kreg[i]);
           bf16x8 hi = __builtin_bit_cast(bf16x8, kreg[i + 1]);
 #pragma unroll
@@ -257,16 +257,22 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
         }
       }
     }
+    // Rows past the end: their scores are masked to -inf, so K needs no
+    // clearing, and P is exactly 0 there; V must then be finite.  fetch()
+    // clamps such rows to the last real row, but the first tile of a
+    // context split is fetched before ctx_len is known, clamped to the
+    // cache's last row, whose contents are arbitrary: only that tile's V
+    // rows past the end are zeroed (a uniform branch).
+    if (!whole && kt == k0 && split < S) {
+#pragma unroll
+      for (int i = 0; i < KLD; ++i)
+        if (kt + ckey[i] >= k1) vreg[i] = make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int i = 0; i < KLD; ++i) {
       const int key = ckey[i], col = ccol[i];
-      uint4 kv = kreg[i], vv = vreg[i];
-      if (!whole && kt + key >= k1) {  // rows past the end stage as zeros
-        kv = make_uint4(0, 0, 0, 0);
-        vv = kv;
-      }
-      *reinterpret_cast<uint4*>(&Ks[key * KP + col]) = kv;
-      *reinterpret_cast<uint4*>(&Vs[key * VP + col]) = vv;
+      *reinterpret_cast<uint4*>(&Ks[key * KP + col]) = kreg[i];
+      *reinterpret_cast<uint4*>(&Vs[key * VP + col]) = vreg[i];
     }
   };
   // transposing-read source of this lane: key offset 4 (lane / 32) +
