@@ -91,8 +91,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
   constexpr int KCH = D / 8;  // 16-byte chunks per key row
   constexpr int TK = kTileKeys * kAttnKH;       // keys staged per iteration
   constexpr int KLD = TK * KCH / kAttnThreads;  // K (and V) chunks per thread
-  __shared__ __align__(16) uint16_t Ks[TK * KP];
-  __shared__ __align__(16) uint16_t Vs[TK * VP];
+  // Two K/V tile buffers (one barrier per tile: a wave stages the next tile
+  // into the other buffer as soon as it is done with the current one); the
+  // rotary variant keeps one, as its tables would not fit beside two
+  constexpr bool kDB = !ROPE;
+  constexpr int NB = kDB ? 2 : 1;
+  __shared__ __align__(16) uint16_t Ks[NB * TK * KP];
+  __shared__ __align__(16) uint16_t Vs[NB * TK * VP];
   __shared__ uint64_t Aw[kAttnWaves * 32 * 16];  // ancestor rows (tree split)
   __shared__ double Rt[ROPE ? D / 2 : 1];         // rotary rate of each pair
   __shared__ int Pk[ROPE ? 1024 : 1];             // position ids of the tree keys
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
       }
     }
   };
-  auto stage = [&](int kt) {
+  auto stage = [&](int kt, uint16_t* kd, uint16_t* vd) {
     const bool whole = kt + TK <= k1;
     if constexpr (ROPE) {
       if (split == S) {  // tree keys: turn each pair at the key's position id
@@ -271,8 +276,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
 #pragma unroll
     for (int i = 0; i < KLD; ++i) {
       const int key = ckey[i], col = ccol[i];
-      *reinterpret_cast<uint4*>(&Ks[key * KP + col]) = kreg[i];
-      *reinterpret_cast<uint4*>(&Vs[key * VP + col]) = vreg[i];
+      *reinterpret_cast<uint4*>(&kd[key * KP + col]) = kreg[i];
+      *reinterpret_cast<uint4*>(&vd[key * VP + col]) = vreg[i];
     }
   };
   // transposing-read source of this lane: key offset 4 (lane / 32) +
@@ -310,11 +315,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
         qf[c + D / 32][e] = (__bf16)(hi * cs + lo * sn);
       }
   }
-  for (int kt0 = k0; kt0 < k1; kt0 += TK) {
-    stage(kt0);
-    lds_barrier();
-    if (kt0 + TK < k1) fetch(kt0 + TK);  // in flight during the products
-
+  // the products and softmax of this wave's 64 keys of the tile at kt0,
+  // staged in (Kt, Vt)
+  auto compute = [&](int kt0, const uint16_t* Kt, const uint16_t* Vt) {
     const int kt = kt0 + kTileKeys * kh;  // this wave's 64 keys: tile rows kr0 ..
     const int kr0 = kTileKeys * kh;
     if (wave_active && kt < k1) {
@@ -345,10 +348,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
         const bf16x8 a0 = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4*>(&Ks[(kr0 + l32) * KP + c * 16 + half * 8]));
+            bf16x8, *reinterpret_cast<const uint4*>(&Kt[(kr0 + l32) * KP + c * 16 + half * 8]));
         const bf16x8 a1 = __builtin_bit_cast(
             bf16x8,
-            *reinterpret_cast<const uint4*>(&Ks[(kr0 + 32 + l32) * KP + c * 16 + half * 8]));
+            *reinterpret_cast<const uint4*>(&Kt[(kr0 + 32 + l32) * KP + c * 16 + half * 8]));
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[c], s1, 0, 0, 0);
       }
@@ -407,7 +410,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
           for (int db = 0; db < D / 32; ++db) {
             // A = V^T: d = 32 db + lane % 32; k-slots 0..3 and 4..7 of the lane
             // are keys 16 t + 4 half + {0..3} and 16 t + 8 + 4 half + {0..3}
-            const uint16_t* vsrc = &Vs[rr * VP + 32 * db + tr_col];
+            const uint16_t* vsrc = &Vt[rr * VP + 32 * db + tr_col];
             const s16x4 lo = lds_read_tr16(vsrc);
             const s16x4 hi = lds_read_tr16(vsrc + 8 * VP);
             const bf16x8 a =
@@ -416,8 +419,35 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
           }
         }
     }
-    lds_barrier();
+  };
+
+  if constexpr (kDB) {
+    // tile t sits in buffer t % 2.  The barrier at the top of an iteration
+    // says that every wave has staged the current tile and finished the
+    // previous one, whose buffer the next tile then takes.
+    if (k0 < k1) {
+      stage(k0, Ks, Vs);
+      if (k0 + TK < k1) fetch(k0 + TK);
+    }
+    int sb = 0;
+    for (int kt0 = k0; kt0 < k1; kt0 += TK, sb ^= 1) {
+      lds_barrier();
+      compute(kt0, Ks + sb * (TK * KP), Vs + sb * (TK * VP));
+      if (kt0 + TK < k1) {
+        stage(kt0 + TK, Ks + (sb ^ 1) * (TK * KP), Vs + (sb ^ 1) * (TK * VP));
+        if (kt0 + 2 * TK < k1) fetch(kt0 + 2 * TK);  // in flight during the next products
+      }
+    }
+  } else {
+    for (int kt0 = k0; kt0 < k1; kt0 += TK) {
+      stage(kt0, Ks, Vs);
+      lds_barrier();
+      if (kt0 + TK < k1) fetch(kt0 + TK);  // in flight during the products
+      compute(kt0, Ks, Vs);
+      lds_barrier();
+    }
   }
+  lds_barrier();  // every tile read done before the buffers serve the exchange
 
   // ---- partials.  The accumulators were last written by an MFMA in the
   // loop body, a different basic block: wait out the result latency before
