@@ -29,6 +29,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "tv_device.h"
 #include "tv_internal.h"
@@ -453,81 +454,90 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
   // loop body, a different basic block: wait out the result latency before
   // the stores read them.
   __builtin_amdgcn_s_sleep(2);
-  // merge the key quarters of each row block: waves kh > 0 hand (O, m, l)
-  // over through LDS (the tiles are free: every wave has passed the loop's
-  // last barrier), stored value-major so that consecutive lanes hit
-  // consecutive banks; wave kh = 0 rescales both to the larger maximum
-  constexpr int NJ = 16 * (D / 32) + 2;  // floats per lane: O, m, l
-  static_assert(2 * NJ * WAVE * 4 <= TK * KP * 2, "exchange fits the K tile");
+  // Merge the key halves of each row block, the two waves splitting the
+  // columns: wave kh keeps columns [kh D/2, (kh + 1) D/2).  Each hands its
+  // (m, l) and the other half of its O to its partner through LDS (the tile
+  // buffers are free: every wave has passed the loop's last barrier),
+  // value-major so that consecutive lanes hit consecutive banks; both then
+  // rescale to the larger maximum, wave 0's terms first so that the two
+  // compute the same l.
+  constexpr int DBH = D / 64;       // accumulator blocks per column half
+  constexpr int NH = 16 * DBH + 2;  // floats per lane handed over: half of O, m, l
+  static_assert(4 * NH * WAVE * 4 <= TK * KP * 2, "exchange fits the K tile");
   static_assert(kAttnKH == 2, "one partner wave per row block");
-  float* xo = reinterpret_cast<float*>(rb < 2 ? Ks : Vs) + (rb & 1) * NJ * WAVE;
-  {
-    if (kh == 1) {
+  float* xbase = reinterpret_cast<float*>(rb < 2 ? Ks : Vs) + (rb & 1) * 2 * NH * WAVE;
+  auto epilogue = [&](auto khc) {
+    constexpr int KH = decltype(khc)::value;
+    constexpr int MINE = KH * DBH, PART = (1 - KH) * DBH;  // accumulator blocks
+    float* xmine = xbase + KH * NH * WAVE;
+    float* xpart = xbase + (1 - KH) * NH * WAVE;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+    for (int e = 0; e < DBH; ++e)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) xo[(db * 16 + i) * WAVE + lane] = oacc[db][i];
-      xo[(NJ - 2) * WAVE + lane] = m_run;
-      xo[(NJ - 1) * WAVE + lane] = l_run;
-    }
+      for (int i = 0; i < 16; ++i) xmine[(e * 16 + i) * WAVE + lane] = oacc[PART + e][i];
+    xmine[(NH - 2) * WAVE + lane] = m_run;
+    xmine[(NH - 1) * WAVE + lane] = l_run;
     lds_barrier();
-    if (kh != 0) return;  // no barrier follows
-    const float mb = xo[(NJ - 2) * WAVE + lane], lb = xo[(NJ - 1) * WAVE + lane];
-    const float mm = fmaxf(m_run, mb);
-    const float aa =
-        m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m_run - mm) * scale_log2);
-    const float ab = mb == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((mb - mm) * scale_log2);
+    const float mp = xpart[(NH - 2) * WAVE + lane], lp = xpart[(NH - 1) * WAVE + lane];
+    const float m0 = KH == 0 ? m_run : mp, m1 = KH == 0 ? mp : m_run;
+    const float l0 = KH == 0 ? l_run : lp, l1 = KH == 0 ? lp : l_run;
+    const float mm = fmaxf(m0, m1);
+    const float a0 = m0 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m0 - mm) * scale_log2);
+    const float a1 = m1 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m1 - mm) * scale_log2);
+    const float am = KH == 0 ? a0 : a1, ap = KH == 0 ? a1 : a0;
+    f32x16 o[DBH];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int e = 0; e < DBH; ++e)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        oacc[db][i] = oacc[db][i] * aa + xo[(db * 16 + i) * WAVE + lane] * ab;
-    l_run = l_run * aa + lb * ab;
-    m_run = mm;
-  }
-  const float l_tot = l_run + xor32_f(l_run);
-  if (row_ok && half == 0) {
-    const int64_t pr = (((int64_t)split * batch + b) * N + node) * Hq + h;
-    Mpart[pr] = m_run * scale_log2;  // log2 domain (-inf stays -inf)
-    Lpart[pr] = l_tot;
-  }
-  // O / l in fp16 (a weighted mean of V rows, so it stays within V's range).
-  // The accumulator gives a lane 4-column runs of one row; the rows go
-  // through this wave's own exchange region (read above, used by no other
-  // wave) so that every store is a whole 16-byte chunk and each store
-  // instruction covers 1 KB of consecutive partial rows.
-  {
-    constexpr int OP = D + 8;  // LDS row pitch (fp16)
-    static_assert(32 * OP * 2 <= NJ * WAVE * 4, "rows fit the exchange region");
-    uint16_t* tw = reinterpret_cast<uint16_t*>(xo);
+        o[e][i] = oacc[MINE + e][i] * am + xpart[(e * 16 + i) * WAVE + lane] * ap;
+    const float lm = l0 * a0 + l1 * a1;
+    const float l_tot = lm + xor32_f(lm);
+    if (KH == 0 && row_ok && half == 0) {
+      const int64_t pr = (((int64_t)split * batch + b) * N + node) * Hq + h;
+      Mpart[pr] = mm * scale_log2;  // log2 domain (-inf stays -inf)
+      Lpart[pr] = l_tot;
+    }
+    // O / l in fp16 (a weighted mean of V rows, so it stays within V's
+    // range).  The accumulator gives a lane 4-column runs of one row; the
+    // rows go through the partner's region (read above, written by no one
+    // else now) so that every store is a whole 16-byte chunk.  A row's
+    // node and head come from the lane that owns it.
+    constexpr int OPH = D / 2 + 8;  // LDS row pitch (fp16)
+    static_assert(32 * OPH * 2 <= NH * WAVE * 4, "rows fit the region");
+    uint16_t* tw = reinterpret_cast<uint16_t*>(xpart);
     const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int e = 0; e < DBH; ++e)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t w2[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const _Float16 x0 = (_Float16)(oacc[db][4 * j + 2 * t] * inv_l);
-          const _Float16 x1 = (_Float16)(oacc[db][4 * j + 2 * t + 1] * inv_l);
+          const _Float16 x0 = (_Float16)(o[e][4 * j + 2 * t] * inv_l);
+          const _Float16 x1 = (_Float16)(o[e][4 * j + 2 * t + 1] * inv_l);
           w2[t] = (uint32_t)__builtin_bit_cast(uint16_t, x0) |
                   ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
         }
-        *reinterpret_cast<uint2*>(&tw[l32 * OP + 32 * db + 8 * j + 4 * half]) =
+        *reinterpret_cast<uint2*>(&tw[l32 * OPH + 32 * e + 8 * j + 4 * half]) =
             make_uint2(w2[0], w2[1]);
       }
-    constexpr int CPR = D / 8;  // 16-byte chunks per row
+    constexpr int CPH = D / 16;  // 16-byte chunks per half row
 #pragma unroll
-    for (int k = 0; k < 32 * CPR / WAVE; ++k) {
-      const int ch = k * WAVE + lane, r = ch / CPR, c16 = ch % CPR;
-      const uint4 x = *reinterpret_cast<const uint4*>(&tw[r * OP + c16 * 8]);
-      const int rowg = row0 + r, nd = rowg / G;
+    for (int k = 0; k < 32 * CPH / WAVE; ++k) {
+      const int ch = k * WAVE + lane, r = ch / CPH, c = ch % CPH;
+      const uint4 x = *reinterpret_cast<const uint4*>(&tw[r * OPH + c * 8]);
+      const int nd = __shfl(node, r), hh = __shfl(h, r);
       if (nd < n) {
-        const int64_t pr = (((int64_t)split * batch + b) * N + nd) * Hq + g * G + rowg % G;
-        *reinterpret_cast<uint4*>(Opart + pr * D + c16 * 8) = x;
+        const int64_t pr = (((int64_t)split * batch + b) * N + nd) * Hq + hh;
+        *reinterpret_cast<uint4*>(Opart + pr * D + KH * (D / 2) + c * 8) = x;
       }
     }
-  }
+  };
+  if (kh == 0)
+    epilogue(std::integral_constant<int, 0>());
+  else
+    epilogue(std::integral_constant<int, 1>());
 }
 
 // Merge the S + 1 partials of every query row.  Partial s holds O_s / l_s in
