@@ -41,6 +41,7 @@
 #include <atomic>
 #include <type_traits>
 
+#include "treeverify.h"
 #include "tv_device.h"
 #include "tv_internal.h"
 
@@ -347,6 +348,7 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int wsum[NT / WAVE];
   __shared__ int s_kept[2];
+  __shared__ int s_total;
   constexpr int NW = NT / WAVE;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
   const int b = blockIdx.x;
@@ -390,13 +392,9 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
   for (int d = 1; d <= K && B > 0; ++d) {
     const double* qd = qtab + (d - 1) * k;
     // ---- candidates: a prefix of every parent's children
-    int total = 0;
-    for (int i0 = 0; i0 < m_par; i0 += NT) {
-      const int i = i0 + tid;
-      const double si = i < m_par ? Ls[i] : 0.0;
-      const int lim = i < m_par ? min(k, B / (i + 1)) : 0;
-      // children that pass form a prefix (scores fall with the rank); the
-      // q values are read eight at a time
+    // children of parent i (score si) that pass form a prefix (scores fall
+    // with the rank); the q values are read eight at a time
+    auto count_children = [&](int i, double si, int lim) {
       int cnt = 0;
       for (int c0 = 0; c0 < k; c0 += 8) {
         double qq[8];
@@ -407,8 +405,9 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
           cnt += (c0 + u < lim && (!have_kappa || si * qq[u] > kappa)) ? 1 : 0;
         if (!__any(cnt == c0 + 8 && c0 + 8 < lim)) break;
       }
-      int tot;
-      const int off = total + block_excl_scan<NT>(cnt, wsum, tot);
+      return cnt;
+    };
+    auto write_children = [&](int i, double si, int cnt, int off) {
       for (int c0 = 0; c0 < cnt; c0 += 8) {
         double qq[8];
 #pragma unroll
@@ -420,11 +419,39 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
             Ck[off + c0 + u] = ((uint32_t)i << 16) | (uint32_t)(c0 + u);
           }
       }
-      total += tot;
+    };
+    int total = 0;
+    if (m_par <= WAVE) {
+      // up to 64 parents: wave 0 alone, with a wave-level scan, so that one
+      // barrier publishes the list and its length
+      if (wave == 0) {
+        const int i = lane;
+        const double si = i < m_par ? Ls[i] : 0.0;
+        const int cnt = count_children(i, si, i < m_par ? min(k, B / (i + 1)) : 0);
+        const int incl = wave_scan_add_dpp(cnt);
+        write_children(i, si, cnt, incl - cnt);
+        if (lane == WAVE - 1) s_total = incl;
+      }
+      __syncthreads();
+      total = s_total;
+      if (total == 0) break;
+      // s_kept[(d + 1) & 1] was last read (as m_par) before this barrier;
+      // the next depth's merge, which counts into it, is barriers away
+      if (tid == 0) s_kept[(d + 1) & 1] = 0;
+    } else {
+      for (int i0 = 0; i0 < m_par; i0 += NT) {
+        const int i = i0 + tid;
+        const double si = i < m_par ? Ls[i] : 0.0;
+        const int cnt = count_children(i, si, i < m_par ? min(k, B / (i + 1)) : 0);
+        int tot;
+        const int off = total + block_excl_scan<NT>(cnt, wsum, tot);
+        write_children(i, si, cnt, off);
+        total += tot;
+      }
+      if (total == 0) break;
+      if (tid == 0) s_kept[(d + 1) & 1] = 0;
+      __syncthreads();
     }
-    if (total == 0) break;
-    if (tid == 0) s_kept[(d + 1) & 1] = 0;
-    __syncthreads();
     const int l = min(total, B);
     if (total <= kRankMax) {
       // ---- level order by rank: wave w counts over its slice of the list
@@ -521,13 +548,15 @@ __global__ __launch_bounds__(NT) void k_select(const int* __restrict__ ftok,
   __syncthreads();
   for (int p = tid; p < g; p += NT) atomicAdd(&dcnt[meta_depth(Gm[p])], 1);
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int dd = 0; dd < K + 2; ++dd) {
-      const int c = dcnt[dd];
-      dcnt[dd] = acc;  // offset of depth dd in `flat`
-      acc += c;
-    }
+  if (wave == 0) {
+    // exclusive prefix over the K + 2 depth counts, two per lane:
+    // dcnt[dd] becomes the offset of depth dd in `flat`
+    static_assert(TV_MAX_POSITIONS + 2 <= 2 * WAVE, "two depth counts per lane");
+    const int e0 = 2 * lane, e1 = e0 + 1;
+    const int c0 = e0 < K + 2 ? dcnt[e0] : 0, c1 = e1 < K + 2 ? dcnt[e1] : 0;
+    const int ex = wave_scan_add_dpp(c0 + c1) - (c0 + c1);
+    if (e0 < K + 2) dcnt[e0] = ex;
+    if (e1 < K + 2) dcnt[e1] = ex + c0;
   }
   __syncthreads();
   for (int p = tid; p < g; p += NT) {
