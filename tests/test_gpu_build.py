@@ -65,6 +65,35 @@ def test_build_ties():
         assert_tree_equal(g, o, s)
 
 
+def test_build_signed_zero_ties():
+    """+0 and -0 are equal logits: their order falls to the token ids."""
+    r = np.random.default_rng(15)
+    K, V, k, B = 4, 9000, 8, 60
+    draft = np.where(r.random((1, K, V)) < 0.5, np.float32(0.0), np.float32(-0.0))
+    draft = draft.astype(np.float32)
+    draft[0, :, ::7] = -1.0
+    g, o = _run(draft, k, B, np.array([3], np.int32), np.array([5], np.int32))
+    assert_tree_equal(g, o, 0)
+
+
+def test_build_nan_logits_finish():
+    """NaN logits are outside the contract (finite, or -inf with a finite
+    row maximum), so the tree they give is unspecified; the call must still
+    finish, with the node count within the budget and the root in row 0."""
+    r = np.random.default_rng(16)
+    K, V, k, B = 6, 20000, 8, 64
+    draft = (r.standard_normal((2, K, V)) * 3).astype(np.float32)
+    draft[0, 1, r.integers(0, V, 40)] = np.nan
+    draft[1, :, 5] = np.nan
+    g = tv.tv_tree_build(dev(draft), k, B, dev(np.array([1, 2], np.int32)),
+                         dev(np.array([10, 20], np.int32)))
+    torch.cuda.synchronize()
+    parent, depth, nn = host(g["parent"]), host(g["depth"]), host(g["n_nodes"])
+    for s in range(2):
+        assert 1 <= int(nn[s]) <= B + 1
+        assert parent[s, 0] == -1 and depth[s, 0] == 0
+
+
 def test_build_neg_inf_and_small_tree():
     r = np.random.default_rng(6)
     K, V, k = 3, 50, 3

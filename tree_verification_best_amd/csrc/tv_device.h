@@ -415,7 +415,10 @@ struct TopkScratch {
   static constexpr int kWaves = NT / WAVE;
   static constexpr int kCap = 256;
   uint64_t sk[kWaves * kCap];  // survivors' keys, per-wave segments
-  uint64_t lk[NT];             // per-thread best keys
+  union {
+    uint64_t lk[NT];  // per-thread best keys
+    float lf[NT];     // or best values
+  };
   int wcount[kWaves];
   int overflow;
   float rv[kWaves];
@@ -430,42 +433,81 @@ __device__ void block_topk(float (&val)[E], int (&id)[E], int k, TopkScratch<NT>
   constexpr int kCap = TopkScratch<NT>::kCap;
   constexpr int kW = NT / WAVE;
   if (tid == 0) sc.overflow = 0;
-  // keys (padding: 0, below every real key) and the per-thread best
-  uint64_t key[E];
-  uint64_t best = 0;
+  // Survivors: the real items at least as good as the wave threshold, the
+  // k-th best of the 64 lane bests (the worst one if fewer than k lanes hold
+  // a real item).  They hold every item of the wave's top k, and only they
+  // are ranked.  Without a NaN in the block the threshold and the test use
+  // the float values (items tied with the threshold survive too), and only
+  // the survivors get keys; with one, the keys decide throughout (their
+  // order puts NaNs outside +-inf, which float compares do not see).
+  float fbest = -__builtin_inff();
+  bool nan_here = false;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    key[e] = id[e] < first_pad ? order_key(val[e], id[e]) : 0ull;
-    best = best > key[e] ? best : key[e];
+    nan_here |= val[e] != val[e];
+    fbest = id[e] < first_pad ? fmaxf(fbest, val[e]) : fbest;
   }
-  // wave threshold: the k-th largest of the 64 lane bests (0 if fewer than
-  // k are real), i.e. the smallest best whose rank is below k
-  sc.lk[tid] = best;
-  __syncthreads();  // also publishes the overflow flag
-  const uint64_t* wk = sc.lk + wave * WAVE;
-  int rank = 0;
+  sc.lf[tid] = fbest;
+  int cnt = 0, incl, total;
+  if (!__syncthreads_or(nan_here)) {  // also publishes the overflow flag
+    const float* wf = sc.lf + wave * WAVE;
+    int rank = 0;
 #pragma unroll
-  for (int j0 = 0; j0 < WAVE; j0 += 16) {
-    uint64_t o[16];
+    for (int j0 = 0; j0 < WAVE; j0 += 16) {
+      float o[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) o[q] = wk[j0 + q];
+      for (int q = 0; q < 16; ++q) o[q] = wf[j0 + q];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) rank += o[q] > best ? 1 : 0;
-  }
-  const uint64_t thr = wave_min_u64(rank < k ? best : ~0ull);
-  // survivors: real items at least as good as the threshold
-  int cnt = 0;
+      for (int q = 0; q < 16; ++q) rank += o[q] > fbest ? 1 : 0;
+    }
+    // the smallest best whose rank is below k (wave minimum as -max(-x))
+    const float thr = -wave_max_f(rank < k ? -fbest : -__builtin_inff());
 #pragma unroll
-  for (int e = 0; e < E; ++e) cnt += (key[e] != 0 && key[e] >= thr) ? 1 : 0;
-  const int incl = wave_incl_scan_i(cnt);
-  const int total = readlane_i(incl, WAVE - 1);
-  if (total > kCap) {
-    if (lane == 0) sc.overflow = 1;
+    for (int e = 0; e < E; ++e) cnt += (id[e] < first_pad && val[e] >= thr) ? 1 : 0;
+    incl = wave_incl_scan_i(cnt);
+    total = readlane_i(incl, WAVE - 1);
+    if (total > kCap) {
+      if (lane == 0) sc.overflow = 1;
+    } else {
+      int off = wave * kCap + incl - cnt;
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (id[e] < first_pad && val[e] >= thr) sc.sk[off++] = order_key(val[e], id[e]);
+    }
   } else {
-    int off = wave * kCap + incl - cnt;
+    // keys (padding: 0, below every real key) and the per-thread best
+    uint64_t key[E];
+    uint64_t best = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (key[e] != 0 && key[e] >= thr) sc.sk[off++] = key[e];
+    for (int e = 0; e < E; ++e) {
+      key[e] = id[e] < first_pad ? order_key(val[e], id[e]) : 0ull;
+      best = best > key[e] ? best : key[e];
+    }
+    sc.lk[tid] = best;
+    __syncthreads();
+    const uint64_t* wk = sc.lk + wave * WAVE;
+    int rank = 0;
+#pragma unroll
+    for (int j0 = 0; j0 < WAVE; j0 += 16) {
+      uint64_t o[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) o[q] = wk[j0 + q];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) rank += o[q] > best ? 1 : 0;
+    }
+    const uint64_t thr = wave_min_u64(rank < k ? best : ~0ull);
+#pragma unroll
+    for (int e = 0; e < E; ++e) cnt += (key[e] != 0 && key[e] >= thr) ? 1 : 0;
+    incl = wave_incl_scan_i(cnt);
+    total = readlane_i(incl, WAVE - 1);
+    if (total > kCap) {
+      if (lane == 0) sc.overflow = 1;
+    } else {
+      int off = wave * kCap + incl - cnt;
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (key[e] != 0 && key[e] >= thr) sc.sk[off++] = key[e];
+    }
   }
   if (lane == 0) sc.wcount[wave] = total;
   __syncthreads();
