@@ -103,16 +103,29 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_partial(
   __shared__ double Rt[ROPE ? D / 2 : 1];         // rotary rate of each pair
   __shared__ int Pk[ROPE ? 1024 : 1];             // position ids of the tree keys
 
-  // unit u = (sequence x KV head, split), split fastest, goes to XCD u % 8;
-  // the XCD's workgroups w = x, x + 8, ... take its units in order, MT
-  // row tiles each
+  // Unit u = (sequence x KV head, split) goes to XCD u % 8; the XCD's
+  // workgroups w = x, x + 8, ... take its units in order, MT row tiles
+  // each.  Units are numbered longest first, so that the workgroups that
+  // start in a later round of the CUs are the short ones: the full context
+  // splits (split fastest), then every unit's last context split (often
+  // shorter), then the tree splits.
   const int w = blockIdx.x;
   const int j = w / 8;
   const int u = w % 8 + 8 * (j / MT);
   if (u >= units) return;  // whole workgroup, before any barrier
   const int mt = j % MT;
-  const int split = u % (S + 1);
-  const int bg = u / (S + 1);
+  const int BG = units / (S + 1);
+  int split, bg;
+  if (u < BG * (S - 1)) {
+    bg = u / (S - 1);
+    split = u % (S - 1);
+  } else if (u < BG * S) {
+    bg = u - BG * (S - 1);
+    split = S - 1;
+  } else {
+    bg = u - BG * S;
+    split = S;
+  }
   const int b = bg / Hkv, g = bg % Hkv;
   const int G = Hq / Hkv;
   // ctx_len <= max_ctx and max_ctx + N <= cap are preconditions; the clamp
