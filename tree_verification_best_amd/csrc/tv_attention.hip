@@ -792,7 +792,7 @@ AttnPlan attention_plan(int batch, int N, int Hq, int Hkv, int D, int max_ctx, i
   int S = splits;
   if (S <= 0) {
     // A cost model fitted to measured times on the 256-CU part: one
-    // workgroup per CU at a time, each paying a fixed ~13 us (launch,
+    // workgroup per CU at a time, each paying a fixed cost (launch,
     // prologue loads, partial stores) plus ~1 us per 64-key tile; then the
     // combine, ~3.5 us plus its partial reads at ~5 TB/s.  One sequence
     // runs in ceil(workgroups / 256) equal rounds.  A batch may hold
@@ -808,7 +808,10 @@ AttnPlan attention_plan(int batch, int N, int Hq, int Hkv, int D, int max_ctx, i
       const int sp = (tiles_ctx + tps - 1) / tps;
       if (sp != c) continue;  // the same as a smaller count
       const int64_t wgs = wg_per_split * (sp + 1);
-      const double per_wg = 13.0 + tps;
+      // fixed cost per workgroup: ~6 us for one sequence (prologue loads and
+      // partial stores, as measured by in-kernel stamps), more for a ragged
+      // batch (its empty splits and uneven rows), both fitted to sweeps
+      const double per_wg = (batch == 1 ? 6.0 : 13.0) + tps;
       const double run = batch == 1 ? (double)((wgs + 255) / 256) * per_wg
                                     : (double)wgs * per_wg / 256.0 + per_wg;
       const double cost = run + 3.5 + part_bytes * (sp + 1) / 5e6;
