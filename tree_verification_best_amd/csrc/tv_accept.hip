@@ -169,13 +169,39 @@ __global__ __launch_bounds__(kAccNT) void k_rowmax(const T* __restrict__ target,
 // that falls in its tokens: wtg[b][x] = W of token(x) in the row of
 // parent(x); in DRAFT mode (wqg non-null) a draft row's block stores
 // wqg[b][x] = W of token(x) in draft row depth(x) - 1.  Ends with a barrier.
-template <typename T, int E>
+// A thread's share of one sequence's tree (nodes 1 + t + 256 k), kept in
+// registers by the pipelined row pass, whose blocks take many rows of the
+// same sequence: the children of each row's node are then found without
+// reloading the tree for every row.
+// Each entry packs the node's token (below 2^18) over its parent (below
+// 2^10): tok << 10 | parent, all ones for no node.
+struct TreeCache {
+  int seq, nn;
+  uint32_t pt[kMaxN / kAccNT];
+};
+
+__device__ __forceinline__ void load_tree(TreeCache& tc, int bb, int N,
+                                          const int* __restrict__ parent,
+                                          const int* __restrict__ token,
+                                          const int* __restrict__ n_nodes) {
+  const int64_t o = (int64_t)bb * N;
+  tc.seq = bb;
+  tc.nn = n_nodes[bb];
+#pragma unroll
+  for (int k = 0; k < kMaxN / kAccNT; ++k) {
+    const int xx = 1 + (int)threadIdx.x + k * kAccNT;
+    tc.pt[k] = xx < N ? ((uint32_t)token[o + xx] << 10) | ((uint32_t)parent[o + xx] & 1023u)
+                      : 0xFFFFFFFFu;
+  }
+}
+
+template <typename T, int E, bool CACHE>
 __device__ __forceinline__ void chunk_mass(const float (&x)[E], const T* p, int V, int C, int cb,
                                            int64_t r, int64_t trows, int64_t rows, float m,
                                            float inv_t, uint64_t* wsum, uint64_t* cz, int N,
                                            int K, const int* parent, const int* token,
                                            const int* depth, const int* n_nodes,
-                                           uint64_t* wtg, uint64_t* wqg) {
+                                           uint64_t* wtg, uint64_t* wqg, TreeCache& tc) {
   static_assert(E % 16 == 0 && E <= 512, "fp64 partial sums must stay exact");
   constexpr int kSpan = E * kAccNT;
   const int base = cb * kSpan;
@@ -200,9 +226,21 @@ __device__ __forceinline__ void chunk_mass(const float (&x)[E], const T* p, int 
       const int64_t j = trow ? r : r - trows;
       const int bb = (int)(j / (trow ? N : K));
       const int uu = (int)(j - (int64_t)bb * (trow ? N : K));
-      const int nn = n_nodes[bb];
       const int64_t o = (int64_t)bb * N;
-      if (nn >= 1 && nn <= N && (!trow || uu < nn)) {
+      if (CACHE && trow) {
+        if (tc.seq != bb) load_tree(tc, bb, N, parent, token, n_nodes);
+        const int nn = tc.nn;
+        if (nn >= 1 && nn <= N && uu < nn) {
+#pragma unroll
+          for (int k = 0; k < kMaxN / kAccNT; ++k) {
+            const int xx = 1 + (int)threadIdx.x + k * kAccNT;
+            const int t = (int)(tc.pt[k] >> 10);
+            if (xx < nn && (int)(tc.pt[k] & 1023u) == uu && t >= base && t < base + kSpan &&
+                t < V)
+              wtg[o + xx] = weight(Elem<T>::load(p, t), m, inv_t);
+          }
+        }
+      } else if (const int nn = n_nodes[bb]; nn >= 1 && nn <= N && (!trow || uu < nn)) {
         for (int xx = 1 + (int)threadIdx.x; xx < nn; xx += kAccNT) {
           const bool mine = trow ? parent[o + xx] == uu : depth[o + xx] == uu + 1;
           if (!mine) continue;
@@ -315,6 +353,12 @@ __global__ __launch_bounds__(kAccNT) void k_rowstat(const T* __restrict__ target
   // this call's slot tag: odd, so never the zero of a new workspace, and
   // different from the previous call's (the walk advances the generation)
   const uint32_t tag = (gen[0] << 1) | 1u;
+  TreeCache tc;
+  tc.seq = -1;
+  if constexpr (PIPE) {
+    // the tree of the first row's sequence, loaded while the row is agreed on
+    if (wtg && r < trows) load_tree(tc, (int)(r / N), N, parent, token, n_nodes);
+  }
   float x[E];
   ChunkLoad<T>::load(row_ptr(target, draft, r, trows, V), cb * kSpan, V, x);
   post_span_max(x, sv, cmax, slot, C, cb, r, rows, slot_stride, tag);
@@ -361,8 +405,8 @@ __global__ __launch_bounds__(kAccNT) void k_rowstat(const T* __restrict__ target
     if constexpr (PIPE) {
       if (rn < rows) post_span_max(y, sv, cmax, slot, C, cb, rn, rows, slot_stride, tag);
     }
-    chunk_mass<T, E>(x, p, V, C, cb, r, trows, rows, m, inv_t, wsum, cz, N, K, parent, token,
-                     depth, n_nodes, wtg, wqg);
+    chunk_mass<T, E, PIPE>(x, p, V, C, cb, r, trows, rows, m, inv_t, wsum, cz, N, K, parent,
+                           token, depth, n_nodes, wtg, wqg, tc);
     // the row's totals for the walk: its maximum, and its mass as the sum of
     // the spans' masses (integer atomics, so the order does not matter).  The
     // last wave sends them: wave 0 polls, and a wave's loads wait for its own
